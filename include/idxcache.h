@@ -1,0 +1,171 @@
+/*
+ * idxcache.h -- C ABI of libidxcache.so: the DeepSeek-Sparse-Attention lightning
+ * indexer with its per-row top-k, the IndexCache Full/Shared layer router, and
+ * sparse MLA attention over the selected latent rows, for AMD MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [ITO] itoverdose.com, "IndexCache: Wie DeepSeek O(NL²)-Kosten in Sparse
+ *         Attention um 75% reduziert"
+ *   [PPM] parapluman.nl, Dutch article on IndexCache, sections "Het DSA-knelpunt"
+ *         and "Aandacht cachen met IndexCache"
+ *   [AIB] aiboss88.com, "IndexCache - 清華大学とZhipuが共同開発した、
+ *         スパースアテンション高速化技術。 - AiBoss", sections "IndexCacheの主な機能"
+ *         and the comparison table "IndexCacheと類似の競合製品との比較"
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises.  Scratch memory is passed in as a
+ *     workspace whose size the matching *_workspace() call reports.
+ *   - Tensors are dense, contiguous, row-major, in the shapes given below.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; results are ready after the
+ *     caller synchronises that stream.
+ *   - Every argument is validated on the host before any HIP call; a failed
+ *     check returns an error code and enqueues nothing.  Launch failures are
+ *     reported as IDXC_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronisation.  No call aborts or throws.
+ *   - Calls keep no state between invocations and may run concurrently on
+ *     different streams with different buffers.
+ */
+#ifndef IDXCACHE_H
+#define IDXCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IDXC_ABI_VERSION 1
+
+typedef enum {
+    IDXC_OK = 0,
+    IDXC_ERR_NULL = -1,        /* a required pointer is NULL */
+    IDXC_ERR_SHAPE = -2,       /* a size is out of range or sizes disagree */
+    IDXC_ERR_DTYPE = -3,       /* unknown encoding or unsupported encoding combination */
+    IDXC_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    IDXC_ERR_UNSUPPORTED = -5, /* valid request this build has no kernel for */
+    IDXC_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required */
+    IDXC_ERR_PATTERN = -7,     /* layer pattern invalid (see idx_cache_route) */
+    IDXC_ERR_HIP = -8          /* the HIP runtime reported an error at launch */
+} idxc_status;
+
+typedef enum {
+    IDXC_BF16 = 1,
+    IDXC_FP8_E4M3 = 2, /* OCP e4m3fn: bias 7, no infinity, max 448 */
+    IDXC_FP32 = 3
+} idxc_dtype;
+
+/*
+ * Lightning indexer problem ([ITO] § "Wie der Indexer funktioniert und warum MLA
+ * entscheidend ist"; [PPM] § "Het DSA-knelpunt"):
+ *   q [B, Lq, H, D]   indexer queries (q_dtype)
+ *   k [B, Lk, D]      indexer keys (k_dtype), one row per cached token
+ *   w [B, Lq, H]      per-query head weights (w_dtype)
+ * Query i of sequence b sits at position p = Lk - Lq + i and scores every key
+ * s <= p:   I[s] = sum_h w[h] * max(0, q[h,:] . k[s,:])   (fp32 accumulation).
+ * Its index set T is the topk keys with the largest I (ties to the lower s),
+ * written in ascending s; a query with p + 1 <= topk gets 0..p and -1 padding.
+ *
+ * Supported: (q,k,w) = (FP8_E4M3, FP8_E4M3, BF16) with D = 128, or
+ * (BF16, BF16, FP32) with D in {32, 64, 128}; H in {4, 8, 16, 32, 64};
+ * 1 <= topk <= 2048; 1 <= Lq <= Lk <= 2^24 - 1; B >= 1.
+ */
+typedef struct {
+    int B, Lq, Lk, H, D, topk;
+    idxc_dtype q_dtype, k_dtype, w_dtype;
+} idxc_indexer_desc;
+
+/* Workspace bytes idx_score_topk / idx_cache_route need for `desc` (may be 0). */
+idxc_status idx_score_topk_workspace(const idxc_indexer_desc *desc, size_t *bytes);
+
+/*
+ * Fused indexer score + per-row top-k ([ITO] § "Einfache Implementierung, enorme
+ * Effizienzgewinne": the Full-layer steps I = Indexer(X), T = top-k(I)).
+ *   t_out      int32 [B, Lq, topk], ascending indices, -1 padded (output)
+ *   scores_dbg optional fp32 [B, Lq, Lk]: if non-NULL, the scores are also
+ *              written there (-inf beyond each query's position).  For tests
+ *              only: it materialises the score matrix the fused path avoids.
+ *   ws, ws_bytes  workspace, at least idx_score_topk_workspace() bytes
+ *              (may be NULL when that size is 0).
+ * Prefill-shaped problems (many queries per sequence) score and select in one
+ * kernel and never store the score matrix; decode-shaped problems (Lq <= 4)
+ * split each sequence's keys over many workgroups and select from the
+ * workspace.  Both give the same T.
+ */
+idxc_status idx_score_topk(const idxc_indexer_desc *desc, const void *q, const void *k,
+                           const void *w, int32_t *t_out, float *scores_dbg, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Workspace bytes for idx_topk (may be 0). */
+idxc_status idx_topk_workspace(int R, int Lk, int topk, size_t *bytes);
+
+/*
+ * Row top-k over given fp32 scores ([ITO] § "Einfache Implementierung, enorme
+ * Effizienzgewinne", the top-k step on its own).
+ *   scores  fp32 [R, Lk]
+ *   row_pos int32 [R] last valid key of each row (keys 0..row_pos[r]); NULL
+ *           means Lk - 1 for every row.  Values must lie in [-1, Lk - 1].
+ *   t_out   int32 [R, topk]: if row_pos + 1 <= topk: 0..row_pos then -1;
+ *           otherwise the topk keys by (score desc, index asc), ascending.
+ * -0 and +0 compare equal.  NaN scores are outside the contract.
+ */
+idxc_status idx_topk(const float *scores, const int32_t *row_pos, int R, int Lk, int topk,
+                     int32_t *t_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * IndexCache layer router ([ITO] §§ "Der unsichtbare Datenstrom" and "Einfache
+ * Implementierung, enorme Effizienzgewinne"; [PPM] § "Aandacht cachen met
+ * IndexCache"; [AIB] comparison table: one branch, no extra GPU memory).
+ *   pattern  NUL-terminated host string, one 'F' (Full) or 'S' (Shared) per
+ *            layer; pattern[0] must be 'F' (the first layer fills the cache).
+ *   layer    0 <= layer < strlen(pattern)
+ *   t_cache  int32 [B, Lq, topk]: the one index buffer shared by all layers.
+ * Full layer: exactly idx_score_topk(desc, q, k, w, t_cache, NULL, ws, ...);
+ *   t_cache is overwritten in place and *computed = 1.
+ * Shared layer: nothing is enqueued, t_cache is left as the nearest preceding
+ *   Full layer wrote it (that layer's T is this layer's T), *computed = 0;
+ *   q, k, w, ws may be NULL.
+ * `computed` is a HOST pointer and may be NULL.
+ */
+idxc_status idx_cache_route(const char *pattern, int layer, const idxc_indexer_desc *desc,
+                            const void *q, const void *k, const void *w, int32_t *t_cache,
+                            void *ws, size_t ws_bytes, void *stream, int *computed);
+
+/*
+ * Sparse MLA attention over the selected rows ([ITO] introduction: attention
+ * over the k selected tokens only; § "Wie der Indexer funktioniert und warum MLA
+ * entscheidend ist": one compressed latent row per token, shared by all heads).
+ *   q   bf16 [B, Lq, Hq, Dqk]
+ *   kv  bf16 [B, Lk, Dqk]   latent rows; keys are the whole row, values are
+ *                           its first Dv columns
+ *   t   int32 [B, Lq, topk] row indices into kv (entries < 0 are skipped;
+ *                           entries must be < Lk)
+ *   out bf16 [B, Lq, Hq, Dv]:  out[h] = sum_j softmax_j(z) kv[t_j, :Dv],
+ *                           z_j = sm_scale * q[h] . kv[t_j]   (fp32 math)
+ *   lse optional fp32 [B, Lq, Hq]: log-sum-exp of z (-inf, with out = 0,
+ *                           for a query whose index set is empty)
+ * Supported: (Dqk, Dv) in {(32, 32), (576, 512)}; Hq a multiple of 4 up to
+ * 128 (Dqk = 32) or a multiple of 16 (Dqk = 576); 1 <= topk <= 2048.
+ */
+typedef struct {
+    int B, Lq, Lk, Hq, Dqk, Dv, topk;
+} idxc_mla_desc;
+
+idxc_status sparse_mla_attn_workspace(const idxc_mla_desc *desc, size_t *bytes);
+
+idxc_status sparse_mla_attn(const idxc_mla_desc *desc, const void *q, const void *kv,
+                            const int32_t *t, float sm_scale, void *out, float *lse, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *idxc_status_str(idxc_status s);
+
+/* IDXC_ABI_VERSION of the loaded library. */
+int idxc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IDXCACHE_H */

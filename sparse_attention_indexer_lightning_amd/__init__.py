@@ -1,0 +1,210 @@
+"""Python binding of libidxcache.so: the lightning indexer with fused top-k, the
+IndexCache Full/Shared router and sparse MLA attention on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  The functions carry
+the names of the C ABI in ``include/idxcache.h``.  Loading fails loudly when
+the library has not been built; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+__all__ = [
+    "IdxcError", "lib", "idx_score_topk", "idx_score_topk_workspace", "idx_topk", "idx_topk_workspace",
+    "idx_cache_route", "sparse_mla_attn", "sparse_mla_attn_workspace", "indexer_desc", "mla_desc",
+    "STATUS", "DTYPE",
+]
+
+STATUS = {0: "IDXC_OK", -1: "IDXC_ERR_NULL", -2: "IDXC_ERR_SHAPE", -3: "IDXC_ERR_DTYPE",
+          -4: "IDXC_ERR_ALIGN", -5: "IDXC_ERR_UNSUPPORTED", -6: "IDXC_ERR_WORKSPACE",
+          -7: "IDXC_ERR_PATTERN", -8: "IDXC_ERR_HIP"}
+DTYPE = {torch.bfloat16: 1, torch.float8_e4m3fn: 2, torch.float32: 3}
+
+
+class IdxcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().idxc_status_str(status).decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg})")
+
+
+class _IndexerDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("B", "Lq", "Lk", "H", "D", "topk", "q_dtype", "k_dtype", "w_dtype")]
+
+
+class _MlaDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("B", "Lq", "Lk", "Hq", "Dqk", "Dv", "topk")]
+
+
+_lib = None
+
+
+def lib():
+    """Load the in-tree libidxcache.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = _build.LIB_PATH
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                              "or python -m sparse_attention_indexer_lightning_amd._build")
+        L = ctypes.CDLL(path)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        szp = ctypes.POINTER(ctypes.c_size_t)
+        ip = ctypes.POINTER(ctypes.c_int)
+        dp = ctypes.POINTER(_IndexerDesc)
+        mp = ctypes.POINTER(_MlaDesc)
+        L.idxc_abi_version.restype = i32
+        L.idxc_abi_version.argtypes = []
+        L.idxc_status_str.restype = ctypes.c_char_p
+        L.idxc_status_str.argtypes = [i32]
+        L.idx_score_topk_workspace.restype = i32
+        L.idx_score_topk_workspace.argtypes = [dp, szp]
+        L.idx_score_topk.restype = i32
+        L.idx_score_topk.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.idx_topk_workspace.restype = i32
+        L.idx_topk_workspace.argtypes = [i32, i32, i32, szp]
+        L.idx_topk.restype = i32
+        L.idx_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, sz, vp]
+        L.idx_cache_route.restype = i32
+        L.idx_cache_route.argtypes = [ctypes.c_char_p, i32, dp, vp, vp, vp, vp, vp, sz, vp, ip]
+        L.sparse_mla_attn_workspace.restype = i32
+        L.sparse_mla_attn_workspace.argtypes = [mp, szp]
+        L.sparse_mla_attn.restype = i32
+        L.sparse_mla_attn.argtypes = [mp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise IdxcError(status, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _cuda_tensor(t, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda):
+        raise TypeError(f"{name} must be a torch tensor on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def indexer_desc(q, k, w, topk: int) -> _IndexerDesc:
+    """Descriptor of an indexer call from q [B,Lq,H,D], k [B,Lk,D], w [B,Lq,H]."""
+    B, Lq, H, D = q.shape
+    Lk = k.shape[1]
+    return _IndexerDesc(B, Lq, Lk, H, D, topk, DTYPE.get(q.dtype, 0), DTYPE.get(k.dtype, 0),
+                        DTYPE.get(w.dtype, 0))
+
+
+def mla_desc(q, kv, t, Dv: int) -> _MlaDesc:
+    B, Lq, Hq, Dqk = q.shape
+    return _MlaDesc(B, Lq, kv.shape[1], Hq, Dqk, Dv, t.shape[-1])
+
+
+def idx_score_topk_workspace(q, k, w, topk: int) -> int:
+    d = indexer_desc(q, k, w, topk)
+    n = ctypes.c_size_t(0)
+    _check(lib().idx_score_topk_workspace(ctypes.byref(d), ctypes.byref(n)), "idx_score_topk_workspace")
+    return n.value
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return ws
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def idx_score_topk(q, k, w, topk: int, t_out=None, scores_dbg=None, ws=None, stream=None):
+    """Fused indexer score + per-row top-k.  Returns T int32 [B, Lq, topk]."""
+    for name, t in (("q", q), ("k", k), ("w", w)):
+        _cuda_tensor(t, name)
+    B, Lq = q.shape[:2]
+    if t_out is None:
+        t_out = torch.empty(B, Lq, topk, dtype=torch.int32, device=q.device)
+    d = indexer_desc(q, k, w, topk)
+    ws = _workspace(idx_score_topk_workspace(q, k, w, topk), q.device, ws)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().idx_score_topk(ctypes.byref(d), _p(q), _p(k), _p(w), _p(t_out), _p(scores_dbg), _p(ws), wsb,
+                                _stream(stream, q.device)), "idx_score_topk")
+    return t_out
+
+
+def idx_topk_workspace(R: int, Lk: int, topk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().idx_topk_workspace(R, Lk, topk, ctypes.byref(n)), "idx_topk_workspace")
+    return n.value
+
+
+def idx_topk(scores, topk: int, row_pos=None, t_out=None, stream=None):
+    """Row top-k of fp32 scores [R, Lk] (ties to the lower index, ascending, -1 padded)."""
+    _cuda_tensor(scores, "scores")
+    R, Lk = scores.shape
+    if t_out is None:
+        t_out = torch.empty(R, topk, dtype=torch.int32, device=scores.device)
+    _check(lib().idx_topk(_p(scores), _p(row_pos), R, Lk, topk, _p(t_out), None, 0,
+                          _stream(stream, scores.device)), "idx_topk")
+    return t_out
+
+
+def idx_cache_route(pattern: str, layer: int, q, k, w, t_cache, topk: int = None, ws=None, stream=None) -> bool:
+    """IndexCache router: Full layers overwrite ``t_cache``; Shared layers enqueue nothing.
+
+    Returns True when the layer computed (Full).  On Shared layers q, k, w may be None.
+    """
+    computed = ctypes.c_int(-1)
+    topk = t_cache.shape[-1] if topk is None else topk
+    pat = pattern.encode()
+    if q is None:
+        d_ptr = None
+        wsb = 0
+        dev = t_cache.device
+    else:
+        d = indexer_desc(q, k, w, topk)
+        d_ptr = ctypes.byref(d)
+        n = ctypes.c_size_t(0)
+        st = lib().idx_score_topk_workspace(d_ptr, ctypes.byref(n))
+        ws = _workspace(n.value if st == 0 else 0, q.device, ws)
+        wsb = 0 if ws is None else ws.numel() * ws.element_size()
+        dev = q.device
+    _check(lib().idx_cache_route(pat, layer, d_ptr, _p(q), _p(k), _p(w), _p(t_cache), _p(ws), wsb,
+                                 _stream(stream, dev), ctypes.byref(computed)), "idx_cache_route")
+    return computed.value == 1
+
+
+def sparse_mla_attn_workspace(q, kv, t, Dv: int) -> int:
+    d = mla_desc(q, kv, t, Dv)
+    n = ctypes.c_size_t(0)
+    _check(lib().sparse_mla_attn_workspace(ctypes.byref(d), ctypes.byref(n)), "sparse_mla_attn_workspace")
+    return n.value
+
+
+def sparse_mla_attn(q, kv, t, sm_scale: float, Dv: int, out=None, lse=None, ws=None, stream=None):
+    """Sparse MLA attention; returns (out bf16 [B,Lq,Hq,Dv], lse fp32 [B,Lq,Hq] or None)."""
+    for name, x in (("q", q), ("kv", kv), ("t", t)):
+        _cuda_tensor(x, name)
+    B, Lq, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty(B, Lq, Hq, Dv, dtype=torch.bfloat16, device=q.device)
+    d = mla_desc(q, kv, t, Dv)
+    ws = _workspace(sparse_mla_attn_workspace(q, kv, t, Dv), q.device, ws)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sparse_mla_attn(ctypes.byref(d), _p(q), _p(kv), _p(t), float(sm_scale), _p(out), _p(lse),
+                                 _p(ws), wsb, _stream(stream, q.device)), "sparse_mla_attn")
+    return out, lse

@@ -1,0 +1,242 @@
+// abi.cpp -- the C ABI of libidxcache.so (declared in include/idxcache.h).
+//
+// Every entry point validates its arguments on the host before the first HIP
+// call, so a rejected call enqueues nothing and needs no GPU.  Dispatch:
+//   idx_score_topk  -> fused prefill kernel (scores never stored), or, for
+//                      decode-shaped problems, split-key scoring into the
+//                      workspace followed by the row top-k kernel;
+//   idx_topk        -> row top-k kernel;
+//   idx_cache_route -> the IndexCache branch (itoverdose.com, "IndexCache: Wie
+//                      DeepSeek O(NL²)-Kosten in Sparse Attention um 75%
+//                      reduziert", section "Einfache Implementierung, enorme
+//                      Effizienzgewinne"): Full layers run idx_score_topk into
+//                      the cache buffer, Shared layers enqueue nothing;
+//   sparse_mla_attn -> sparse MLA kernel.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/idxcache.h"
+#include "kernels.h"
+
+using idxc::Enc;
+
+namespace {
+
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxLen = (1 << 24) - 1;
+constexpr int kDecodeMaxLq = 4;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool known_dtype(int d) { return d == IDXC_BF16 || d == IDXC_FP8_E4M3 || d == IDXC_FP32; }
+
+bool h_supported(int H) { return H == 4 || H == 8 || H == 16 || H == 32 || H == 64; }
+
+// Shape/encoding checks shared by idx_score_topk and idx_cache_route.
+idxc_status check_indexer_desc(const idxc_indexer_desc *d) {
+    if (!d) return IDXC_ERR_NULL;
+    if (!known_dtype(d->q_dtype) || !known_dtype(d->k_dtype) || !known_dtype(d->w_dtype)) return IDXC_ERR_DTYPE;
+    const bool fp8 = d->q_dtype == IDXC_FP8_E4M3 && d->k_dtype == IDXC_FP8_E4M3 && d->w_dtype == IDXC_BF16;
+    const bool bf16 = d->q_dtype == IDXC_BF16 && d->k_dtype == IDXC_BF16 && d->w_dtype == IDXC_FP32;
+    if (!fp8 && !bf16) return IDXC_ERR_DTYPE;
+    if (d->B < 1 || d->Lq < 1 || d->Lk < 1 || d->Lq > d->Lk || d->H < 1 || d->D < 1 || d->topk < 1)
+        return IDXC_ERR_SHAPE;
+    if (d->Lk > kMaxLen) return IDXC_ERR_SHAPE;
+    if ((size_t)d->B * (size_t)d->Lk > (size_t)INT32_MAX) return IDXC_ERR_SHAPE;
+    if (!h_supported(d->H) || d->topk > kMaxTopk) return IDXC_ERR_UNSUPPORTED;
+    if (fp8 && d->D != 128) return IDXC_ERR_UNSUPPORTED;
+    if (bf16 && d->D != 32 && d->D != 64 && d->D != 128) return IDXC_ERR_UNSUPPORTED;
+    return IDXC_OK;
+}
+
+idxc::IndexerArgs make_args(const idxc_indexer_desc *d, const void *q, const void *k, const void *w,
+                            int32_t *t, float *scores) {
+    idxc::IndexerArgs a;
+    a.q = q; a.k = k; a.w = w; a.t_out = t; a.scores = scores;
+    a.B = d->B; a.Lq = d->Lq; a.Lk = d->Lk; a.H = d->H; a.D = d->D; a.topk = d->topk;
+    a.qk_enc = d->q_dtype == IDXC_FP8_E4M3 ? Enc::FP8 : Enc::BF16;
+    a.w_enc = d->w_dtype == IDXC_BF16 ? Enc::BF16 : Enc::FP32;
+    return a;
+}
+
+enum class Path { Fused, Decode, None };
+
+Path choose_path(const idxc::IndexerArgs &a) {
+    if (a.Lq <= kDecodeMaxLq && idxc::decode_supported(a)) return Path::Decode;
+    if (idxc::prefill_fits(a)) return Path::Fused;
+    if (idxc::decode_supported(a)) return Path::Decode;
+    return Path::None;
+}
+
+size_t decode_ws_bytes(const idxc_indexer_desc *d) {
+    return (size_t)d->B * d->Lq * d->Lk * sizeof(float);
+}
+
+idxc_status from_hip(hipError_t e) { return e == hipSuccess ? IDXC_OK : IDXC_ERR_HIP; }
+
+// Validation of the tensors of an F-layer call; shared by score_topk and route.
+idxc_status check_indexer_call(const idxc_indexer_desc *d, const void *q, const void *k, const void *w,
+                               const int32_t *t, const float *scores_dbg, const void *ws, size_t ws_bytes,
+                               Path *path) {
+    idxc_status st = check_indexer_desc(d);
+    if (st != IDXC_OK) return st;
+    if (!q || !k || !w || !t) return IDXC_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(t, 16) || !aligned(w, 4)) return IDXC_ERR_ALIGN;
+    if (scores_dbg && !aligned(scores_dbg, 16)) return IDXC_ERR_ALIGN;
+    const idxc::IndexerArgs a = make_args(d, q, k, w, nullptr, nullptr);
+    *path = choose_path(a);
+    if (*path == Path::None) return IDXC_ERR_UNSUPPORTED;
+    if (*path == Path::Decode) {
+        if (!ws || ws_bytes < decode_ws_bytes(d)) return IDXC_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return IDXC_ERR_ALIGN;
+    }
+    return IDXC_OK;
+}
+
+idxc_status run_indexer(const idxc_indexer_desc *d, const void *q, const void *k, const void *w, int32_t *t,
+                        float *scores_dbg, void *ws, Path path, hipStream_t stream) {
+    if (path == Path::Fused) {
+        idxc::IndexerArgs a = make_args(d, q, k, w, t, scores_dbg);
+        return from_hip(idxc::launch_indexer_prefill(a, stream));
+    }
+    float *scores = static_cast<float *>(ws);
+    idxc::IndexerArgs a = make_args(d, q, k, w, t, scores);
+    hipError_t e = idxc::launch_indexer_scores(a, stream);
+    if (e != hipSuccess) return IDXC_ERR_HIP;
+    idxc::TopkArgs ta;
+    ta.scores = scores;
+    ta.row_pos = nullptr;
+    ta.R = d->B * d->Lq;
+    ta.Lk = d->Lk;
+    ta.topk = d->topk;
+    ta.pos_Lq = d->Lq;
+    ta.t_out = t;
+    e = idxc::launch_row_topk(ta, stream);
+    if (e != hipSuccess) return IDXC_ERR_HIP;
+    if (scores_dbg)
+        e = hipMemcpyAsync(scores_dbg, scores, decode_ws_bytes(d), hipMemcpyDeviceToDevice, stream);
+    return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int idxc_abi_version(void) { return IDXC_ABI_VERSION; }
+
+const char *idxc_status_str(idxc_status s) {
+    switch (s) {
+    case IDXC_OK: return "ok";
+    case IDXC_ERR_NULL: return "a required pointer is NULL";
+    case IDXC_ERR_SHAPE: return "a size is out of range or sizes disagree";
+    case IDXC_ERR_DTYPE: return "unknown or unsupported element encoding combination";
+    case IDXC_ERR_ALIGN: return "a pointer is not suitably aligned";
+    case IDXC_ERR_UNSUPPORTED: return "no kernel for this valid request";
+    case IDXC_ERR_WORKSPACE: return "workspace missing or too small";
+    case IDXC_ERR_PATTERN: return "invalid layer pattern or layer index";
+    case IDXC_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+idxc_status idx_score_topk_workspace(const idxc_indexer_desc *desc, size_t *bytes) {
+    if (!bytes) return IDXC_ERR_NULL;
+    idxc_status st = check_indexer_desc(desc);
+    if (st != IDXC_OK) return st;
+    const idxc::IndexerArgs a = make_args(desc, nullptr, nullptr, nullptr, nullptr, nullptr);
+    const Path p = choose_path(a);
+    if (p == Path::None) return IDXC_ERR_UNSUPPORTED;
+    *bytes = p == Path::Decode ? decode_ws_bytes(desc) : 0;
+    return IDXC_OK;
+}
+
+idxc_status idx_score_topk(const idxc_indexer_desc *desc, const void *q, const void *k, const void *w,
+                           int32_t *t_out, float *scores_dbg, void *ws, size_t ws_bytes, void *stream) {
+    Path path;
+    idxc_status st = check_indexer_call(desc, q, k, w, t_out, scores_dbg, ws, ws_bytes, &path);
+    if (st != IDXC_OK) return st;
+    return run_indexer(desc, q, k, w, t_out, scores_dbg, ws, path, static_cast<hipStream_t>(stream));
+}
+
+idxc_status idx_topk_workspace(int R, int Lk, int topk, size_t *bytes) {
+    if (!bytes) return IDXC_ERR_NULL;
+    if (R < 0 || Lk < 1 || topk < 1 || Lk > kMaxLen) return IDXC_ERR_SHAPE;
+    if (topk > kMaxTopk) return IDXC_ERR_UNSUPPORTED;
+    *bytes = 0;
+    return IDXC_OK;
+}
+
+idxc_status idx_topk(const float *scores, const int32_t *row_pos, int R, int Lk, int topk, int32_t *t_out,
+                     void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (R < 0 || Lk < 1 || topk < 1 || Lk > kMaxLen) return IDXC_ERR_SHAPE;
+    if (topk > kMaxTopk) return IDXC_ERR_UNSUPPORTED;
+    if (R == 0) return IDXC_OK;
+    if (!scores || !t_out) return IDXC_ERR_NULL;
+    if (!aligned(scores, 4) || !aligned(t_out, 4) || (row_pos && !aligned(row_pos, 4))) return IDXC_ERR_ALIGN;
+    idxc::TopkArgs a;
+    a.scores = scores;
+    a.row_pos = row_pos;
+    a.R = R;
+    a.Lk = Lk;
+    a.topk = topk;
+    a.pos_Lq = 0;
+    a.t_out = t_out;
+    return from_hip(idxc::launch_row_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+idxc_status idx_cache_route(const char *pattern, int layer, const idxc_indexer_desc *desc, const void *q,
+                            const void *k, const void *w, int32_t *t_cache, void *ws, size_t ws_bytes,
+                            void *stream, int *computed) {
+    if (!pattern || !t_cache) return IDXC_ERR_NULL;
+    const size_t n = strlen(pattern);
+    if (n == 0 || pattern[0] != 'F') return IDXC_ERR_PATTERN;
+    for (size_t i = 0; i < n; ++i)
+        if (pattern[i] != 'F' && pattern[i] != 'S') return IDXC_ERR_PATTERN;
+    if (layer < 0 || (size_t)layer >= n) return IDXC_ERR_PATTERN;
+    if (pattern[layer] == 'S') {
+        // T of this layer is the cache as the nearest preceding Full layer left it.
+        if (computed) *computed = 0;
+        return IDXC_OK;
+    }
+    Path path;
+    idxc_status st = check_indexer_call(desc, q, k, w, t_cache, nullptr, ws, ws_bytes, &path);
+    if (st != IDXC_OK) return st;
+    st = run_indexer(desc, q, k, w, t_cache, nullptr, ws, path, static_cast<hipStream_t>(stream));
+    if (st == IDXC_OK && computed) *computed = 1;
+    return st;
+}
+
+idxc_status sparse_mla_attn_workspace(const idxc_mla_desc *desc, size_t *bytes) {
+    if (!desc || !bytes) return IDXC_ERR_NULL;
+    *bytes = 0;
+    return IDXC_OK;
+}
+
+idxc_status sparse_mla_attn(const idxc_mla_desc *desc, const void *q, const void *kv, const int32_t *t,
+                            float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!desc) return IDXC_ERR_NULL;
+    const idxc_mla_desc &d = *desc;
+    if (d.B < 1 || d.Lq < 1 || d.Lk < 1 || d.Hq < 1 || d.Dqk < 1 || d.Dv < 1 || d.topk < 1 || d.Dv > d.Dqk)
+        return IDXC_ERR_SHAPE;
+    if (d.Lk > kMaxLen || (size_t)d.B * d.Lq > (size_t)INT32_MAX / 2) return IDXC_ERR_SHAPE;
+    const bool small = d.Dqk == 32 && d.Dv == 32;
+    const bool mla = d.Dqk == 576 && d.Dv == 512;
+    if (!small && !mla) return IDXC_ERR_UNSUPPORTED;
+    if (small && (d.Hq % 4 != 0 || d.Hq > 128)) return IDXC_ERR_UNSUPPORTED;
+    if (mla && d.Hq % 16 != 0) return IDXC_ERR_UNSUPPORTED;
+    if (d.topk > kMaxTopk) return IDXC_ERR_UNSUPPORTED;
+    if (!(sm_scale > 0.f) || sm_scale > 1e30f) return IDXC_ERR_SHAPE;
+    if (!q || !kv || !t || !out) return IDXC_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(t, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)))
+        return IDXC_ERR_ALIGN;
+    idxc::MlaArgs a;
+    a.q = q; a.kv = kv; a.t = t; a.out = out; a.lse = lse; a.sm_scale = sm_scale;
+    a.B = d.B; a.Lq = d.Lq; a.Lk = d.Lk; a.Hq = d.Hq; a.Dqk = d.Dqk; a.Dv = d.Dv; a.topk = d.topk;
+    return from_hip(idxc::launch_sparse_mla(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// device_common.h -- wavefront helpers and MFMA wrappers for gfx950 (CDNA4).
+// Internal to libidxcache; every kernel here runs 64-lane wavefronts.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idxc {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+// number of set bits of `m` in lanes below the calling lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Orders the LDS traffic of one wavefront: later LDS reads see earlier writes
+// by any lane of the same wavefront.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Order-preserving 32-bit key of a score: larger key <=> larger float,
+// with -0 and +0 mapped to the same key.  NaN is outside the contract.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// D(16x16, fp32) = A(16x128, fp8 e4m3) * B(128x16, fp8 e4m3) + C.
+// Lane l supplies row/column l%16 and the 32 k-values 32*(l/16)..+31 of A/B;
+// it receives D[4*(l/16)+i][l%16], i = 0..3.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i &a, const v8i &b, const v4f &c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D(16x16, fp32) = A(16x32, bf16) * B(32x16, bf16) + C.
+// Lane l supplies row/column l%16 and k-values 8*(l/16)..+7; output as above.
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf &a, const v8bf &b, const v4f &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) { return __shfl_xor(v, m, kWave); }
+
+}  // namespace idxc

@@ -1,0 +1,604 @@
+// indexer.hip -- lightning indexer scores on MFMA with the per-row top-k fused in.
+//
+// Score (itoverdose.com, "IndexCache: Wie DeepSeek O(NL²)-Kosten in Sparse
+// Attention um 75% reduziert", section "Wie der Indexer funktioniert und warum
+// MLA entscheidend ist"; parapluman.nl, section "Het DSA-knelpunt"):
+//     I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]),   s <= position(t)
+// followed by the top-k of each row (same page, section "Einfache
+// Implementierung, enorme Effizienzgewinne").
+//
+// Prefill kernel (many queries per sequence).  One workgroup owns R
+// consecutive query rows of one sequence and sweeps that sequence's keys in
+// blocks of 64, staging each key block in LDS.  Each wavefront holds its rows'
+// queries as MFMA A-fragments (64 (row, head) pairs = four 16-row fragments)
+// in registers for the whole sweep; per 16-key sub-block it issues four MFMAs
+// (fp8 16x16x128, or bf16 16x16x32 per 32-wide slice of d).  The ReLU and the
+// head-weighted sum run on the fp32 accumulators in registers; the head sum
+// finishes with a two-step cross-lane transpose-reduce that leaves lane l
+// holding the score of key (block + l).  Scores never reach HBM.
+//
+// Streaming top-k.  Each row owns an LDS candidate buffer of `cap` entries
+// (order-preserving 32-bit score key + key index) and a threshold key.  A key
+// enters the buffer when its key is strictly above the threshold; appends go
+// in ascending key order (ballot + prefix count), so the buffer stays sorted
+// by index.  When the buffer cannot take another block, the owning wavefront
+// finds the exact k-th largest key by MSB-first radix select (8-bit digits,
+// LDS histogram) and keeps, in place and in order, every entry above it plus
+// the lowest-index entries equal to it, then raises the threshold to it.
+// Keys equal to the threshold that arrive later have larger indices and can
+// never displace a kept entry, so strict ">" is exact.  At the end one more
+// selection leaves exactly min(k, p+1) entries, already in ascending order.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace idxc {
+namespace {
+
+constexpr int KB = 64;          // keys per block (one per lane after the reduce)
+constexpr int kMaxThreads = 512;
+constexpr int kChunkMax = 4;    // 16-byte chunks each thread stages per key block
+
+template <Enc E, int D>
+struct Shape {
+    static constexpr int EB = (E == Enc::FP8) ? 1 : 2;    // bytes per element
+    static constexpr int ROWB = D * EB;                    // bytes per key row
+    static constexpr int PITCH = ROWB + 16;                // LDS row pitch
+    static constexpr int NV = (E == Enc::FP8) ? 2 : D / 32; // 16-byte pieces per lane
+};
+
+// One lane's share of a 16-row x D operand (A or B of the MFMA).
+template <Enc E, int D>
+struct Frag {
+    v4i x[Shape<E, D>::NV];
+};
+
+// byte offset of piece v of lane group g inside one row
+template <Enc E, int D>
+__device__ __forceinline__ int piece_off(int v, int g) {
+    if constexpr (E == Enc::FP8) return 32 * g + 16 * v;
+    else return 64 * v + 16 * g;
+}
+
+template <Enc E, int D>
+__device__ __forceinline__ void load_frag(Frag<E, D> &f, const unsigned char *row, int g) {
+#pragma unroll
+    for (int v = 0; v < Shape<E, D>::NV; ++v)
+        f.x[v] = *reinterpret_cast<const v4i *>(row + piece_off<E, D>(v, g));
+}
+
+template <Enc E, int D>
+__device__ __forceinline__ void zero_frag(Frag<E, D> &f) {
+#pragma unroll
+    for (int v = 0; v < Shape<E, D>::NV; ++v) f.x[v] = v4i{0, 0, 0, 0};
+}
+
+template <Enc E, int D>
+__device__ __forceinline__ v4f frag_mma(const Frag<E, D> &a, const Frag<E, D> &b) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (E == Enc::FP8) {
+        v8i av = __builtin_shufflevector(a.x[0], a.x[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        v8i bv = __builtin_shufflevector(b.x[0], b.x[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = mfma_fp8_16x16x128(av, bv, acc);
+    } else {
+#pragma unroll
+        for (int v = 0; v < Shape<E, D>::NV; ++v)
+            acc = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, a.x[v]), __builtin_bit_cast(v8bf, b.x[v]), acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float load_w(const void *w, Enc enc, size_t idx) {
+    if (enc == Enc::BF16) return bf16_to_f32(reinterpret_cast<const uint16_t *>(w)[idx]);
+    return reinterpret_cast<const float *>(w)[idx];
+}
+
+// Lane group g holds partial sums p[j] of sub-block j for the same 16 keys as
+// the other three groups; returns the full sum of sub-block g.
+__device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2, float p3, int g) {
+    const bool lo = g < 2;
+    float ka = lo ? p0 : p2, kb = lo ? p1 : p3;
+    const float sa = lo ? p2 : p0, sb = lo ? p3 : p1;
+    ka += shfl_xor(sa, 32);
+    kb += shfl_xor(sb, 32);
+    const bool odd = (g & 1) != 0;
+    const float keep = odd ? kb : ka, send = odd ? ka : kb;
+    return keep + shfl_xor(send, 16);
+}
+
+// ---------------------------------------------------------------- selection
+
+// Exact k-th largest key among buf_key[0..cnt) (cnt >= k), then in-place
+// stable compaction to the k best (ties: lowest index = earliest entry).
+// Wave-level; `hist` is this wave's 256-entry LDS scratch.
+template <typename IdxT>
+__device__ void select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, uint32_t &thr, int k, uint32_t *hist,
+                               int lane) {
+    uint32_t prefix = 0, pmask = 0;
+    int need = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int j = lane; j < 256; j += kWave) hist[j] = 0;
+        wave_lds_sync();
+        for (int i = lane; i < cnt; i += kWave) {
+            const uint32_t u = bkey[i];
+            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        }
+        wave_lds_sync();
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+                       h3 = hist[4 * lane + 3];
+        const uint32_t s = h0 + h1 + h2 + h3;
+        uint32_t S = s;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t v = __shfl_down(S, o, kWave);
+            if (lane + o < kWave) S += v;
+        }
+        const uint32_t E = S - s;
+        const bool here = (E < (uint32_t)need) && (S >= (uint32_t)need);
+        int bsel;
+        uint32_t above;
+        {
+            uint32_t c = E;
+            if (c + h3 >= (uint32_t)need) { bsel = 3; above = c; }
+            else {
+                c += h3;
+                if (c + h2 >= (uint32_t)need) { bsel = 2; above = c; }
+                else {
+                    c += h2;
+                    if (c + h1 >= (uint32_t)need) { bsel = 1; above = c; }
+                    else { c += h1; bsel = 0; above = c; }
+                }
+            }
+        }
+        const uint64_t m = ballot(here);
+        const int src = __builtin_ctzll(m);
+        const int bin = __shfl(4 * lane + bsel, src, kWave);
+        const uint32_t ab = __shfl(above, src, kWave);
+        prefix |= (uint32_t)bin << shift;
+        pmask |= 0xFFu << shift;
+        need -= (int)ab;
+    }
+    wave_lds_sync();
+    // keep: key > prefix, or key == prefix among the first `need` such entries
+    int out = 0, eqseen = 0;
+    for (int base = 0; base < cnt; base += kWave) {
+        const int i = base + lane;
+        uint32_t u = 0;
+        IdxT ix = 0;
+        if (i < cnt) { u = bkey[i]; ix = bidx[i]; }
+        const bool gt = i < cnt && u > prefix;
+        const bool eq = i < cnt && u == prefix;
+        const uint64_t em = ballot(eq);
+        const int erank = eqseen + lanes_below(em);
+        const bool keep = gt || (eq && erank < need);
+        const uint64_t km = ballot(keep);
+        const int pos = out + lanes_below(km);
+        wave_lds_sync();
+        if (keep) { bkey[pos] = u; bidx[pos] = ix; }
+        wave_lds_sync();
+        out += __popcll(km);
+        eqseen += __popcll(em);
+    }
+    cnt = out;
+    thr = prefix;
+}
+
+struct PrefillParams {
+    const unsigned char *q, *k;
+    const void *w;
+    int32_t *t_out;
+    float *scores;
+    int B, Lq, Lk, topk, cap;
+    Enc w_enc;
+};
+
+// LDS plan of the prefill kernel; identical on host and device.
+struct PrefillLds {
+    size_t ktile, stage, hist, state, bkey, bidx, total;
+};
+
+__host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, int cap, int idx_bytes, bool staged) {
+    PrefillLds L;
+    const int R = waves * tw;
+    L.ktile = 0;
+    size_t off = (size_t)2 * KB * pitch;
+    L.stage = off;
+    off += staged ? (size_t)waves * tw * KB * 4 : 0;
+    L.hist = off;
+    off += (size_t)waves * 256 * 4;
+    L.state = off;
+    off += (size_t)R * 8;
+    L.bkey = off;
+    off += (size_t)R * cap * 4;
+    off = (off + 15) & ~(size_t)15;
+    L.bidx = off;
+    off += (size_t)R * cap * idx_bytes;
+    L.total = (off + 15) & ~(size_t)15;
+    return L;
+}
+
+template <Enc E, int D, int H, typename IdxT>
+__global__ __launch_bounds__(kMaxThreads) void prefill_kernel(PrefillParams p) {
+    using S = Shape<E, D>;
+    constexpr int TW = 64 / H;              // query rows per wave
+    constexpr bool kStaged = H < 16;        // scores go through LDS before selection
+    const int waves = blockDim.x / kWave;
+    const int R = waves * TW;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4, n = lane & 15;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    const PrefillLds L = prefill_lds(waves, TW, S::PITCH, p.cap, (int)sizeof(IdxT), kStaged);
+    unsigned char *ktile = smem + L.ktile;
+    float *stage = reinterpret_cast<float *>(smem + L.stage) + (size_t)wave * TW * KB;
+    uint32_t *hist = reinterpret_cast<uint32_t *>(smem + L.hist) + wave * 256;
+    int *rcnt = reinterpret_cast<int *>(smem + L.state);
+    uint32_t *rthr = reinterpret_cast<uint32_t *>(smem + L.state) + R;
+    uint32_t *bkey_all = reinterpret_cast<uint32_t *>(smem + L.bkey);
+    IdxT *bidx_all = reinterpret_cast<IdxT *>(smem + L.bidx);
+
+    // heaviest row blocks (largest positions) are dispatched first
+    const int nrb = (p.Lq + R - 1) / R;
+    const int rb = nrb - 1 - (int)(blockIdx.x / p.B);
+    const int b = (int)(blockIdx.x % p.B);
+    const int i0 = rb * R;
+    const int off = p.Lk - p.Lq;
+    const int pmax = off + min(i0 + R, p.Lq) - 1;
+    const int nblk = pmax / KB + 1;
+
+    // A fragments: fragment f, row r = 16f + n -> (t, h) = (r / H, r % H)
+    Frag<E, D> A[4];
+    float wv[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const int r = 16 * f + n, t = r / H, h = r % H;
+        const int i = i0 + wave * TW + t;
+        if (i < p.Lq) {
+            const size_t qrow = ((size_t)(b * (size_t)p.Lq + i) * H + h) * S::ROWB;
+            load_frag<E, D>(A[f], p.q + qrow, g);
+        } else {
+            zero_frag<E, D>(A[f]);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int ro = 16 * f + 4 * g + ii, to = ro / H, ho = ro % H;
+            const int io = i0 + wave * TW + to;
+            wv[f][ii] = io < p.Lq ? load_w(p.w, p.w_enc, ((size_t)b * p.Lq + io) * H + ho) : 0.f;
+        }
+    }
+    for (int t = lane; t < TW; t += kWave) {
+        rcnt[wave * TW + t] = 0;
+        rthr[wave * TW + t] = 0u;
+    }
+
+    // stage key block 0
+    const int nchunk = KB * S::ROWB / 16;
+    v4i kreg[kChunkMax];
+    auto fetch = [&](int blk) {
+#pragma unroll
+        for (int c = 0; c < kChunkMax; ++c) {
+            const int ci = tid + c * (int)blockDim.x;
+            kreg[c] = v4i{0, 0, 0, 0};
+            if (ci < nchunk) {
+                const int key = blk * KB + ci / (S::ROWB / 16);
+                if (key < p.Lk)
+                    kreg[c] = *reinterpret_cast<const v4i *>(
+                        p.k + ((size_t)b * p.Lk + key) * S::ROWB + (ci % (S::ROWB / 16)) * 16);
+            }
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < kChunkMax; ++c) {
+            const int ci = tid + c * (int)blockDim.x;
+            if (ci < nchunk)
+                *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + (ci / (S::ROWB / 16)) * S::PITCH +
+                                         (ci % (S::ROWB / 16)) * 16) = kreg[c];
+        }
+    };
+    fetch(0);
+    stash(0);
+    __syncthreads();
+
+    // last position among this wave's valid rows (for skipping blocks)
+    const int wlast = min(i0 + wave * TW + TW, p.Lq) - 1;
+    const int wpmax = off + wlast;
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int cur = blk & 1;
+        if (blk + 1 < nblk) fetch(blk + 1);
+        const int base = blk * KB;
+        if (wlast >= i0 + wave * TW && base <= wpmax) {
+            const unsigned char *kt = ktile + (size_t)cur * KB * S::PITCH;
+            v4f acc[4][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                Frag<E, D> Bf;
+                load_frag<E, D>(Bf, kt + (16 * j + n) * S::PITCH, g);
+#pragma unroll
+                for (int f = 0; f < 4; ++f) acc[j][f] = frag_mma<E, D>(A[f], Bf);
+            }
+            float sc[TW];
+            if constexpr (!kStaged) {
+                // rows of fragment f all belong to query t = f * 16 / H
+                float part[TW][4];
+#pragma unroll
+                for (int t = 0; t < TW; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) part[t][j] = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        const int t = (16 * f) / H;
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            part[t][j] += wv[f][ii] * fmaxf(acc[j][f][ii], 0.f);
+                    }
+#pragma unroll
+                for (int t = 0; t < TW; ++t)
+                    sc[t] = transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3], g);
+            } else {
+                // H = 4: lane group g holds all heads of query 4f+g;
+                // H = 8: groups g and g^1 hold the two halves of query 2f+g/2.
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) {
+                        float s = 0.f;
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) s += wv[f][ii] * fmaxf(acc[j][f][ii], 0.f);
+                        if constexpr (H == 8) {
+                            s += shfl_xor(s, 16);
+                            if ((g & 1) == 0) stage[(2 * f + (g >> 1)) * KB + 16 * j + n] = s;
+                        } else {
+                            stage[(4 * f + g) * KB + 16 * j + n] = s;
+                        }
+                    }
+                wave_lds_sync();
+#pragma unroll
+                for (int t = 0; t < TW; ++t) sc[t] = stage[t * KB + lane];
+                wave_lds_sync();
+            }
+            // selection, one row at a time
+#pragma unroll
+            for (int t = 0; t < TW; ++t) {
+                const int i = i0 + wave * TW + t;
+                if (i >= p.Lq) continue;
+                const int pos = off + i;
+                if (base > pos) continue;
+                const int s = base + lane;
+                const int row = wave * TW + t;
+                if (p.scores && s < p.Lk)
+                    p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc[t] : -INFINITY;
+                int cnt = rcnt[row];
+                uint32_t thr = rthr[row];
+                const uint32_t key = score_key(sc[t]);
+                const bool cand = s <= pos && key > thr;
+                const uint64_t m = ballot(cand);
+                if (m) {
+                    uint32_t *bk = bkey_all + (size_t)row * p.cap;
+                    IdxT *bi = bidx_all + (size_t)row * p.cap;
+                    const int at = cnt + lanes_below(m);
+                    if (cand) { bk[at] = key; bi[at] = (IdxT)s; }
+                    cnt += __popcll(m);
+                    wave_lds_sync();
+                    if (cnt > p.cap - KB) select_compact<IdxT>(bk, bi, cnt, thr, p.topk, hist, lane);
+                    if (lane == 0) { rcnt[row] = cnt; rthr[row] = thr; }
+                    wave_lds_sync();
+                }
+            }
+        }
+        __syncthreads();
+        if (blk + 1 < nblk) stash(cur ^ 1);
+        __syncthreads();
+    }
+
+    // final selection and output
+    for (int t = 0; t < TW; ++t) {
+        const int i = i0 + wave * TW + t;
+        if (i >= p.Lq) break;
+        const int row = wave * TW + t;
+        int cnt = rcnt[row];
+        uint32_t thr = rthr[row];
+        uint32_t *bk = bkey_all + (size_t)row * p.cap;
+        IdxT *bi = bidx_all + (size_t)row * p.cap;
+        if (cnt > p.topk) select_compact<IdxT>(bk, bi, cnt, thr, p.topk, hist, lane);
+        int32_t *o = p.t_out + ((size_t)b * p.Lq + i) * p.topk;
+        for (int j = lane; j < p.topk; j += kWave) o[j] = j < cnt ? (int32_t)bi[j] : -1;
+        if (p.scores) {
+            const int pos = off + i;
+            for (int s = (pos / KB + 1) * KB + lane; s < p.Lk; s += kWave)
+                p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- decode scores
+
+struct ScoreParams {
+    const unsigned char *q, *k;
+    const void *w;
+    float *scores;
+    int B, Lq, Lk, split;
+    Enc w_enc;
+};
+
+constexpr int kDecodeWaves = 4;
+
+// 64 heads of one query against a contiguous key range; B operands are read
+// straight from HBM (each key is used by exactly one query row here).
+template <Enc E, int D>
+__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(ScoreParams p) {
+    using S = Shape<E, D>;
+    constexpr int H = 64;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4, n = lane & 15;
+    const int row = blockIdx.y;
+    const int b = row / p.Lq, i = row % p.Lq;
+    const int pos = p.Lk - p.Lq + i;
+    const int s0 = blockIdx.x * p.split;
+    const int s1 = min(s0 + p.split, p.Lk);
+    float *out = p.scores + (size_t)row * p.Lk;
+
+    Frag<E, D> A[4];
+    float wv[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        load_frag<E, D>(A[f], p.q + ((size_t)row * H + 16 * f + n) * S::ROWB, g);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) wv[f][ii] = load_w(p.w, p.w_enc, (size_t)row * H + 16 * f + 4 * g + ii);
+    }
+    const unsigned char *kb = p.k + (size_t)b * p.Lk * S::ROWB;
+    for (int base = s0 + wave * KB; base < s1; base += kDecodeWaves * KB) {
+        const int s = base + lane;
+        if (base > pos) {
+            if (s < s1) out[s] = -INFINITY;
+            continue;
+        }
+        Frag<E, D> Bf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int key = base + 16 * j + n;
+            if (key < p.Lk) load_frag<E, D>(Bf[j], kb + (size_t)key * S::ROWB, g);
+            else zero_frag<E, D>(Bf[j]);
+        }
+        float part[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            part[j] = 0.f;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const v4f a = frag_mma<E, D>(A[f], Bf[j]);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) part[j] += wv[f][ii] * fmaxf(a[ii], 0.f);
+            }
+        }
+        const float sc = transpose_reduce4(part[0], part[1], part[2], part[3], g);
+        if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
+    }
+}
+
+template <Enc E, int D, int H, typename IdxT>
+hipError_t launch_prefill_t(const IndexerArgs &a, int waves, int cap, size_t lds, hipStream_t st) {
+    auto kern = prefill_kernel<E, D, H, IdxT>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    PrefillParams p;
+    p.q = static_cast<const unsigned char *>(a.q);
+    p.k = static_cast<const unsigned char *>(a.k);
+    p.w = a.w;
+    p.t_out = a.t_out;
+    p.scores = a.scores;
+    p.B = a.B; p.Lq = a.Lq; p.Lk = a.Lk; p.topk = a.topk; p.cap = cap;
+    p.w_enc = a.w_enc;
+    const int R = waves * (64 / H);
+    const int nrb = (a.Lq + R - 1) / R;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(nrb * a.B)), dim3(waves * kWave), lds, st, p);
+    return hipGetLastError();
+}
+
+struct PrefillPlan {
+    int waves, cap, idx_bytes;
+    size_t lds;
+    bool ok;
+};
+
+constexpr size_t kLdsBudget = 160 * 1024;
+
+PrefillPlan plan_prefill(const IndexerArgs &a) {
+    PrefillPlan pl{0, 0, 0, 0, false};
+    const int eb = a.qk_enc == Enc::FP8 ? 1 : 2;
+    const int rowb = a.D * eb, pitch = rowb + 16;
+    const int tw = 64 / a.H;
+    const bool staged = a.H < 16;
+    pl.idx_bytes = a.Lk <= 65536 ? 2 : 4;
+    const int nchunk = KB * rowb / 16;
+    int min_waves = (nchunk + kChunkMax * kWave - 1) / (kChunkMax * kWave);
+    if (min_waves < 1) min_waves = 1;
+    for (int waves = 8; waves >= min_waves; waves /= 2) {
+        // room beyond k: at least one block of appends (KB); more room means
+        // fewer re-selections per row.  Take the most LDS allows, up to 1024.
+        for (int slack = 1024; slack >= KB; slack /= 2) {
+            const int cap = a.topk + slack;
+            const PrefillLds L = prefill_lds(waves, tw, pitch, cap, pl.idx_bytes, staged);
+            if (L.total <= kLdsBudget) {
+                pl.waves = waves;
+                pl.cap = cap;
+                pl.lds = L.total;
+                pl.ok = true;
+                return pl;
+            }
+        }
+        if (waves == 1) break;
+    }
+    return pl;
+}
+
+template <Enc E, int D, int H>
+hipError_t launch_prefill_h(const IndexerArgs &a, hipStream_t st) {
+    const PrefillPlan pl = plan_prefill(a);
+    if (!pl.ok) return hipErrorInvalidConfiguration;
+    if (pl.idx_bytes == 2) return launch_prefill_t<E, D, H, uint16_t>(a, pl.waves, pl.cap, pl.lds, st);
+    return launch_prefill_t<E, D, H, uint32_t>(a, pl.waves, pl.cap, pl.lds, st);
+}
+
+template <Enc E, int D>
+hipError_t launch_prefill_d(const IndexerArgs &a, hipStream_t st) {
+    switch (a.H) {
+    case 4: return launch_prefill_h<E, D, 4>(a, st);
+    case 8: return launch_prefill_h<E, D, 8>(a, st);
+    case 16: return launch_prefill_h<E, D, 16>(a, st);
+    case 32: return launch_prefill_h<E, D, 32>(a, st);
+    case 64: return launch_prefill_h<E, D, 64>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <Enc E, int D>
+hipError_t launch_decode_d(const IndexerArgs &a, hipStream_t st) {
+    ScoreParams p;
+    p.q = static_cast<const unsigned char *>(a.q);
+    p.k = static_cast<const unsigned char *>(a.k);
+    p.w = a.w;
+    p.scores = a.scores;
+    p.B = a.B; p.Lq = a.Lq; p.Lk = a.Lk;
+    p.split = 4096;
+    p.w_enc = a.w_enc;
+    const int nsplit = (a.Lk + p.split - 1) / p.split;
+    hipLaunchKernelGGL((decode_scores_kernel<E, D>), dim3((unsigned)nsplit, (unsigned)(a.B * a.Lq)),
+                       dim3(kDecodeWaves * kWave), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_fits(const IndexerArgs &a) { return plan_prefill(a).ok; }
+
+hipError_t launch_indexer_prefill(const IndexerArgs &a, hipStream_t st) {
+    if (a.qk_enc == Enc::FP8) {
+        if (a.D == 128) return launch_prefill_d<Enc::FP8, 128>(a, st);
+    } else if (a.qk_enc == Enc::BF16) {
+        if (a.D == 32) return launch_prefill_d<Enc::BF16, 32>(a, st);
+        if (a.D == 64) return launch_prefill_d<Enc::BF16, 64>(a, st);
+        if (a.D == 128) return launch_prefill_d<Enc::BF16, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool decode_supported(const IndexerArgs &a) {
+    if (a.H != 64) return false;
+    if (a.qk_enc == Enc::FP8) return a.D == 128;
+    return a.D == 32 || a.D == 64 || a.D == 128;
+}
+
+hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t st) {
+    if (a.qk_enc == Enc::FP8) {
+        if (a.D == 128) return launch_decode_d<Enc::FP8, 128>(a, st);
+    } else if (a.qk_enc == Enc::BF16) {
+        if (a.D == 32) return launch_decode_d<Enc::BF16, 32>(a, st);
+        if (a.D == 64) return launch_decode_d<Enc::BF16, 64>(a, st);
+        if (a.D == 128) return launch_decode_d<Enc::BF16, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace idxc

@@ -1,0 +1,52 @@
+// kernels.h -- internal launch interface between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace idxc {
+
+enum class Enc : int { BF16 = 1, FP8 = 2, FP32 = 3 };
+
+struct IndexerArgs {
+    const void *q, *k, *w;
+    int32_t *t_out;
+    float *scores;   // prefill: optional debug copy; decode: required score rows
+    int B, Lq, Lk, H, D, topk;
+    Enc qk_enc, w_enc;
+};
+
+// Fused score + streaming top-k for prefill-shaped problems.  Returns
+// hipErrorInvalidConfiguration when the shape does not fit the kernel's LDS
+// plan (the caller then takes the two-step path).
+bool prefill_fits(const IndexerArgs &a);
+hipError_t launch_indexer_prefill(const IndexerArgs &a, hipStream_t s);
+
+// Scores of every (query, key <= position) into a.scores [B*Lq, Lk], keys
+// split over many workgroups; -inf beyond each query's position.
+bool decode_supported(const IndexerArgs &a);
+hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t s);
+
+// Exact per-row top-k of fp32 scores [R, Lk] (ties to the lower index,
+// ascending output, -1 padding).  row_pos may be NULL (all Lk keys valid).
+// pos_from_query != 0 derives the position of row r as (Lk - Lq + r % Lq).
+struct TopkArgs {
+    const float *scores;
+    const int32_t *row_pos;
+    int R, Lk, topk;
+    int pos_Lq;       // > 0: row position = Lk - pos_Lq + r % pos_Lq (row_pos unused)
+    int32_t *t_out;
+};
+hipError_t launch_row_topk(const TopkArgs &a, hipStream_t s);
+
+struct MlaArgs {
+    const void *q, *kv;
+    const int32_t *t;
+    void *out;
+    float *lse;
+    float sm_scale;
+    int B, Lq, Lk, Hq, Dqk, Dv, topk;
+};
+hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);
+
+}  // namespace idxc

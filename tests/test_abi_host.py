@@ -1,0 +1,166 @@
+"""The C ABI on the host: the library loads, exports every declared entry point,
+and rejects every invalid request before any HIP call (so no GPU is needed).
+
+Pointers passed here are fake, 16-byte-aligned addresses: each call below must
+fail validation, which happens before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_lightning_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idxcache.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, PATTERN = 0, -1, -2, -3, -4, -5, -6, -7
+BF16, FP8, FP32 = 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x10008)   # 8-byte aligned only
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:idxc_status|const char \*|int)\s+(\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = sa.lib()
+    names = declared_functions()
+    assert {"idx_score_topk", "idx_topk", "idx_cache_route", "sparse_mla_attn"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.idxc_abi_version() == 1
+
+
+def test_status_strings():
+    L = sa.lib()
+    for code in range(-8, 1):
+        assert L.idxc_status_str(code)
+    assert L.idxc_status_str(5) == b"unknown status"
+
+
+def desc(B=1, Lq=128, Lk=128, H=64, D=128, topk=64, qd=FP8, kd=FP8, wd=BF16):
+    return sa._IndexerDesc(B, Lq, Lk, H, D, topk, qd, kd, wd)
+
+
+def score(d, q=FAKE, k=FAKE, w=FAKE, t=FAKE, dbg=None, ws=None, wsb=0):
+    return sa.lib().idx_score_topk(ctypes.byref(d) if d is not None else None, q, k, w, t, dbg, ws, wsb, None)
+
+
+def ws_bytes(d):
+    n = ctypes.c_size_t(0)
+    st = sa.lib().idx_score_topk_workspace(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qd=9), DTYPE), (dict(wd=0), DTYPE),
+    (dict(qd=FP8, kd=BF16), DTYPE), (dict(qd=BF16, kd=BF16, wd=BF16), DTYPE),
+    (dict(qd=FP8, kd=FP8, wd=FP32), DTYPE),
+    (dict(B=0), SHAPE), (dict(Lq=0), SHAPE), (dict(Lq=200, Lk=100), SHAPE), (dict(H=0), SHAPE),
+    (dict(topk=0), SHAPE), (dict(Lk=1 << 24, Lq=1), SHAPE),
+    (dict(H=12), UNSUP), (dict(H=128), UNSUP), (dict(topk=2049), UNSUP), (dict(D=64), UNSUP),
+    (dict(qd=BF16, kd=BF16, wd=FP32, D=48), UNSUP),
+])
+def test_indexer_descriptor_rejections(kw, code):
+    d = desc(**kw)
+    assert score(d) == code
+    assert ws_bytes(d)[0] == code
+
+
+def test_indexer_pointer_and_alignment_rejections():
+    d = desc()
+    assert score(None) == NULL
+    assert score(d, q=None) == NULL
+    assert score(d, k=None) == NULL
+    assert score(d, w=None) == NULL
+    assert score(d, t=None) == NULL
+    assert score(d, q=FAKE_ODD) == ALIGN
+    assert score(d, k=FAKE_ODD) == ALIGN
+    assert score(d, t=FAKE_ODD) == ALIGN
+    assert score(d, dbg=FAKE_ODD) == ALIGN
+    assert score(d, w=ctypes.c_void_p(0x10002)) == ALIGN
+
+
+def test_workspace_sizes_and_rejections():
+    # prefill-shaped: fused kernel, no workspace
+    assert ws_bytes(desc(Lq=8192, Lk=8192, topk=2048)) == (OK, 0)
+    assert ws_bytes(desc(Lq=65536, Lk=65536, topk=2048)) == (OK, 0)
+    # decode-shaped: one fp32 score row per query
+    d = desc(B=32, Lq=1, Lk=200000, topk=2048)
+    st, n = ws_bytes(d)
+    assert st == OK and n == 32 * 200000 * 4
+    assert score(d) == WS
+    assert score(d, ws=FAKE, wsb=n - 1) == WS
+    assert score(d, ws=FAKE_ODD, wsb=n) == ALIGN
+    # small head counts need more query rows per workgroup than LDS holds at large k
+    assert ws_bytes(desc(qd=BF16, kd=BF16, wd=FP32, H=4, D=32, topk=2048, Lq=4096, Lk=4096))[0] == UNSUP
+    assert ws_bytes(desc(qd=BF16, kd=BF16, wd=FP32, H=4, D=32, topk=64, Lq=512, Lk=512)) == (OK, 0)
+
+
+def test_topk_rejections():
+    L = sa.lib()
+    assert L.idx_topk(FAKE, None, 4, 0, 8, FAKE, None, 0, None) == SHAPE
+    assert L.idx_topk(FAKE, None, -1, 10, 8, FAKE, None, 0, None) == SHAPE
+    assert L.idx_topk(FAKE, None, 4, 10, 0, FAKE, None, 0, None) == SHAPE
+    assert L.idx_topk(FAKE, None, 4, 10, 4096, FAKE, None, 0, None) == UNSUP
+    assert L.idx_topk(None, None, 4, 10, 8, FAKE, None, 0, None) == NULL
+    assert L.idx_topk(FAKE, None, 4, 10, 8, None, None, 0, None) == NULL
+    assert L.idx_topk(ctypes.c_void_p(0x10001), None, 4, 10, 8, FAKE, None, 0, None) == ALIGN
+    assert L.idx_topk(FAKE, None, 0, 10, 8, FAKE, None, 0, None) == OK  # nothing to do
+    n = ctypes.c_size_t(7)
+    assert L.idx_topk_workspace(4, 10, 8, ctypes.byref(n)) == OK and n.value == 0
+
+
+def route(pattern, layer, d=None, q=FAKE, k=FAKE, w=FAKE, t=FAKE):
+    c = ctypes.c_int(-1)
+    st = sa.lib().idx_cache_route(pattern, layer, ctypes.byref(d) if d is not None else None,
+                                  q, k, w, t, None, 0, None, ctypes.byref(c))
+    return st, c.value
+
+
+def test_router_pattern_rules():
+    for pat, layer in ((b"SFFF", 0), (b"SFFF", 1), (b"FSXS", 1), (b"", 0), (b"FS", 2), (b"FS", -1), (b"fS", 0)):
+        assert route(pat, layer, desc())[0] == PATTERN, (pat, layer)
+    assert route(None, 0, desc())[0] == NULL
+    assert route(b"FS", 0, desc(), t=None)[0] == NULL
+
+
+def test_router_shared_layer_enqueues_nothing():
+    # Shared layers need neither inputs nor a descriptor and touch no device state.
+    for layer in (1, 2, 3):
+        assert route(b"FSSS", layer, None, q=None, k=None, w=None) == (OK, 0)
+    assert route(b"FSFS", 3, None, q=None, k=None, w=None) == (OK, 0)
+
+
+def test_router_full_layer_validates_like_score_topk():
+    assert route(b"FSSS", 0, None)[0] == NULL
+    assert route(b"FSSS", 0, desc(qd=7))[0] == DTYPE
+    assert route(b"FSSS", 0, desc(), q=FAKE_ODD)[0] == ALIGN
+    assert route(b"FS", 0, desc(B=32, Lq=1, Lk=200000, topk=2048))[0] == WS
+
+
+def mla(B=1, Lq=4, Lk=100, Hq=128, Dqk=576, Dv=512, topk=64, scale=0.04, q=FAKE, kv=FAKE, t=FAKE, out=FAKE):
+    d = sa._MlaDesc(B, Lq, Lk, Hq, Dqk, Dv, topk)
+    return sa.lib().sparse_mla_attn(ctypes.byref(d), q, kv, t, scale, out, None, None, 0, None)
+
+
+def test_sparse_mla_rejections():
+    assert sa.lib().sparse_mla_attn(None, FAKE, FAKE, FAKE, 1.0, FAKE, None, None, 0, None) == NULL
+    assert mla(B=0) == SHAPE
+    assert mla(Dv=600) == SHAPE
+    assert mla(scale=0.0) == SHAPE
+    assert mla(scale=float("nan")) == SHAPE
+    assert mla(Dqk=128, Dv=128) == UNSUP
+    assert mla(Hq=24) == UNSUP
+    assert mla(Dqk=32, Dv=32, Hq=6) == UNSUP
+    assert mla(topk=4096) == UNSUP
+    assert mla(q=None) == NULL
+    assert mla(kv=None) == NULL
+    assert mla(t=None) == NULL
+    assert mla(out=None) == NULL
+    assert mla(q=FAKE_ODD) == ALIGN
+    assert mla(kv=FAKE_ODD) == ALIGN

@@ -1,0 +1,167 @@
+"""GPU parity of the indexer + top-k and the router, through the C ABI, on small
+and edge-case shapes the oracle computes in full."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_indexer_lightning_amd as sa
+from sparse_attention_indexer_lightning_amd import inputs
+from parity_util import (RTOL, check_index_sets, check_scores, check_t_invariants_gpu, enc_of,
+                         indexer_oracle)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_full(q, k, w, topk, dbg=True):
+    B, Lq = q.shape[:2]
+    Lk = k.shape[1]
+    scores = torch.empty(B, Lq, Lk, dtype=torch.float32, device=DEV) if dbg else None
+    t = sa.idx_score_topk(q, k, w, topk, scores_dbg=scores)
+    torch.cuda.synchronize()
+    return t, scores
+
+
+def compare_all_rows(q, k, w, topk, what, exact_sets=False):
+    B, Lq = q.shape[:2]
+    Lk = k.shape[1]
+    t, scores = run_full(q, k, w, topk)
+    to, so = indexer_oracle(q, k, w, topk)
+    rt = RTOL[enc_of(q)]
+    check_scores(scores.cpu().numpy().reshape(B * Lq, Lk), so, rt, what)
+    tg = t.cpu().numpy().reshape(B * Lq, topk)
+    pos = oracle.row_positions(B, Lq, Lk)
+    if exact_sets:
+        assert np.array_equal(tg, to), what
+    else:
+        check_index_sets(tg, to, so, pos, topk, rt, what)
+    check_t_invariants_gpu(t, Lq, Lk, topk)
+    return tg, to
+
+
+def _golden():
+    with open(os.path.join(GOLDEN, "hand_example_8tok.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("enc,H,D", [("fp8", 64, 128), ("bf16", 4, 32), ("bf16", 16, 64)])
+def test_hand_example_through_router(enc, H, D):
+    g = _golden()
+    L, k = g["L"], g["topk"]
+    qdt = torch.float8_e4m3fn if enc == "fp8" else torch.bfloat16
+    wdt = torch.bfloat16 if enc == "fp8" else torch.float32
+    keys = torch.zeros(1, L, D)
+    keys[0, :, :2] = torch.tensor(g["keys"], dtype=torch.float32)
+    q = torch.zeros(1, L, H, D)
+    q[0, :, 0, 0] = 1.0
+    q[0, :, 1, 1] = 1.0
+    t_cache = torch.full((1, L, k), 12345, dtype=torch.int32, device=DEV)
+    for layer, c in enumerate(g["pattern"]):
+        ww = g["w_even_odd_by_layer"][str(layer)]
+        w = torch.zeros(1, L, H)
+        for t in range(L):
+            w[0, t, :2] = torch.tensor(ww["even"] if t % 2 == 0 else ww["odd"], dtype=torch.float32)
+        before = t_cache.clone()
+        did = sa.idx_cache_route(g["pattern"], layer, q.to(qdt).to(DEV), keys.to(qdt).to(DEV),
+                                 w.to(wdt).to(DEV), t_cache)
+        torch.cuda.synchronize()
+        assert did == (c == "F")
+        if c == "S":
+            assert torch.equal(before, t_cache), "a Shared layer modified the cache"
+        src = g["expected"]["T_by_layer"][str(layer)]
+        assert t_cache[0].cpu().tolist() == g["expected"][src]["T"], (enc, layer)
+
+
+@pytest.mark.parametrize("enc,H,D", [("bf16", 4, 32), ("bf16", 8, 32), ("bf16", 16, 64), ("bf16", 32, 128),
+                                     ("bf16", 64, 32), ("fp8", 16, 128), ("fp8", 32, 128), ("fp8", 64, 128)])
+def test_head_counts_and_dims(enc, H, D):
+    wl = inputs.Workload("t", 1, 300, 300, H, D, 40, enc, "bf16" if enc == "fp8" else "fp32", 11)
+    q, k, w = inputs.indexer_inputs(wl, 0, DEV)
+    compare_all_rows(q, k, w, 40, f"{enc} H={H} D={D}")
+
+
+@pytest.mark.parametrize("B,Lq,Lk,topk", [
+    (1, 50, 50, 64),        # every row shorter than k: pure padding
+    (1, 777, 777, 100),     # ragged length, several key blocks
+    (3, 130, 130, 17),      # batch
+    (1, 300, 1000, 256),    # chunked prefill: queries at the end of a longer context
+    (1, 200, 200, 1),       # k = 1
+    (2, 3, 5000, 300),      # decode-shaped (split-key path) with B > 1, Lq > 1
+    (1, 1, 3000, 2048),     # single decode query
+])
+def test_edge_shapes_fp8(B, Lq, Lk, topk):
+    wl = inputs.Workload("e", B, Lq, Lk, 64, 128, topk, "fp8", "bf16", 5)
+    q, k, w = inputs.indexer_inputs(wl, 0, DEV)
+    compare_all_rows(q, k, w, topk, f"B={B} Lq={Lq} Lk={Lk} k={topk}")
+
+
+def test_long_context_32bit_indices():
+    """Lk > 65536 switches the candidate buffers to 32-bit indices."""
+    wl = inputs.Workload("l", 1, 40, 70000, 64, 128, 2048, "fp8", "bf16", 6)
+    q, k, w = inputs.indexer_inputs(wl, 0, DEV)
+    t, scores = run_full(q, k, w, 2048)
+    rows = np.array([0, 17, 39], dtype=np.int64)
+    to, so = indexer_oracle(q, k, w, 2048, rows=rows)
+    sg = scores.cpu().numpy().reshape(40, -1)[rows]
+    check_scores(sg, so, RTOL["fp8"], "Lk=70000")
+    pos = oracle.row_positions(1, 40, 70000, rows)
+    check_index_sets(t.cpu().numpy().reshape(40, -1)[rows], to, so, pos, 2048, RTOL["fp8"], "Lk=70000")
+
+
+@pytest.mark.parametrize("enc", ["fp8", "bf16"])
+@pytest.mark.parametrize("kind", ["recency", "reverse", "ties", "negzero_ties"])
+@pytest.mark.parametrize("Lq,Lk", [(700, 700), (2, 9000)])
+def test_closed_forms(enc, kind, Lq, Lk):
+    """Scores with a known order: recency (I = s) inserts every key into the
+    streaming selection, reverse (I = -s) only the first k; ties must resolve
+    to the lowest indices, also when every score is -0."""
+    H, D, k = (64, 128, 256) if enc == "fp8" else (4, 32, 64)
+    q, kk, w = inputs.closed_form_indexer(1, Lk, H, D, enc, kind, device=DEV)
+    q = q[:, Lk - Lq:].contiguous()
+    w = w[:, Lk - Lq:].contiguous()
+    t, scores = run_full(q, kk, w, k)
+    tg = t.cpu().numpy().reshape(Lq, k)
+    sg = scores.cpu().numpy().reshape(Lq, Lk)
+    for i in range(Lq):
+        p = Lk - Lq + i
+        n = min(k, p + 1)
+        if kind == "recency":
+            want = np.arange(p + 1 - n, p + 1)
+            assert np.array_equal(sg[i, : p + 1], np.arange(p + 1, dtype=np.float32))
+        else:
+            want = np.arange(n)
+        assert np.array_equal(tg[i, :n], want), (kind, i)
+        assert np.all(tg[i, n:] == -1)
+        assert np.all(np.isneginf(sg[i, p + 1:]))
+
+
+def test_determinism():
+    wl = inputs.Workload("d", 1, 1500, 1500, 64, 128, 512, "fp8", "bf16", 9)
+    q, k, w = inputs.indexer_inputs(wl, 0, DEV)
+    t1, s1 = run_full(q, k, w, 512)
+    t2, s2 = run_full(q, k, w, 512)
+    t3, _ = run_full(q, k, w, 512, dbg=False)
+    assert torch.equal(t1, t2) and torch.equal(t1, t3)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def test_fused_and_split_paths_agree():
+    """The fused prefill kernel and the split-key path select the same sets."""
+    wl = inputs.Workload("a", 2, 4, 6000, 64, 128, 700, "fp8", "bf16", 12)
+    q, k, w = inputs.indexer_inputs(wl, 0, DEV)
+    t_split, s_split = run_full(q, k, w, 700)           # Lq <= 4: split-key path
+    # the same queries as the tail of a longer query block: fused path
+    wl2 = inputs.Workload("a", 2, 40, 6000, 64, 128, 700, "fp8", "bf16", 12)
+    q2 = torch.zeros(2, 40, 64, 128, dtype=q.dtype, device=DEV)
+    w2 = torch.zeros(2, 40, 64, dtype=w.dtype, device=DEV)
+    q2[:, 36:] = q
+    w2[:, 36:] = w
+    t_fused, s_fused = run_full(q2.contiguous(), k, w2.contiguous(), 700)
+    assert torch.equal(t_split, t_fused[:, 36:])
+    assert torch.equal(s_split, s_fused[:, 36:])
+    del wl2

@@ -1,0 +1,68 @@
+"""GPU parity of sparse MLA attention against the oracle (max-abs <= 2e-2 on the
+bf16 output, log-sum-exp within 1e-3)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_indexer_lightning_amd as sa
+from parity_util import raw
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+ATOL = 2e-2
+
+
+def _bf16_np(x: torch.Tensor) -> np.ndarray:
+    return oracle.bf16_bits_to_f64(raw(x))
+
+
+def run_and_compare(B, Lq, Lk, Hq, Dqk, Dv, k, t_kind="random", seed=0):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    q = torch.randn(B, Lq, Hq, Dqk, generator=g, device=DEV).to(torch.bfloat16)
+    kv = torch.randn(B, Lk, Dqk, generator=g, device=DEV).to(torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    t = np.full((B, Lq, k), -1, np.int32)
+    for b in range(B):
+        for i in range(Lq):
+            if t_kind == "random":
+                n = int(rng.integers(0, min(k, Lk) + 1))
+                t[b, i, :n] = rng.choice(Lk, size=n, replace=False)
+                rng.shuffle(t[b, i])
+            elif t_kind == "full":
+                n = min(k, Lk)
+                t[b, i, :n] = rng.choice(Lk, size=n, replace=False)
+    tt = torch.from_numpy(t).to(DEV)
+    scale = 1.0 / math.sqrt(Dqk)
+    lse = torch.empty(B, Lq, Hq, dtype=torch.float32, device=DEV)
+    out, _ = sa.sparse_mla_attn(q, kv, tt, scale, Dv, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_mla_dv(raw(q), raw(kv), t, scale, Dv)
+    go = _bf16_np(out).reshape(ro.shape)
+    err = np.abs(go - oracle.bf16_bits_to_f64(ro)).max()
+    assert err <= ATOL, f"max-abs error {err}"
+    gl = lse.cpu().numpy().reshape(rl.shape)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.allclose(gl[fin], rl[fin], rtol=1e-4, atol=1e-3)
+    return err
+
+
+@pytest.mark.parametrize("Hq", [4, 8, 20])
+def test_small_latent(Hq):
+    run_and_compare(2, 33, 400, Hq, 32, 32, 64)
+
+
+@pytest.mark.parametrize("Hq,k", [(16, 64), (128, 200), (32, 2048)])
+def test_mla_latent(Hq, k):
+    run_and_compare(1, 3, 3000, Hq, 576, 512, k, seed=Hq)
+
+
+def test_mla_full_index_sets():
+    run_and_compare(2, 2, 5000, 128, 576, 512, 2048, t_kind="full", seed=3)
+
+
+def test_empty_index_set():
+    run_and_compare(1, 2, 100, 16, 576, 512, 64, t_kind="empty")
