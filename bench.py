@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the lightning-indexer hot path on one MI355X.
+
+Headline (``value``): scored causal (query, key) pairs per second of the fused
+indexer + top-k at L = 65536 (H_I = 64, d_I = 128, k = 2048, fp8 q/k, bf16 w),
+one step = one Full layer routed through ``idx_cache_route`` (score, ReLU,
+head-weighted sum, causal mask and per-row top-k in one kernel, T written).
+
+Secondary (``secondary``): the 200K-context decode step (32 sequences, one query
+each): Full layer = indexer + top-k + sparse MLA, Shared layer = sparse MLA
+only, and a 4-layer F,S,S,S group against an all-Full group, in decode tokens
+per second; plus the gather bandwidth of sparse MLA.
+
+``roofline``: the fused indexer kernel against the fp8 MFMA peak; ``achieved``
+is algorithmic flops (pairs x H x D x 2) over the average launch time measured
+with HIP events on the launch stream.  ``traffic`` comes from rocprofv3 counter
+runs committed under profiles/ (null when not measured for this kernel build).
+
+``cpu_baseline``: the plain fp64 CPU oracle on a bounded seeded sample of query
+rows of the same workload, in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_prefill_64k_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
+    ap.add_argument("--profile-only", action="store_true", help="run warmup+steps of the headline only")
+    return ap.parse_args()
+
+
+def causal_pairs(Lq: int, Lk: int, B: int = 1) -> int:
+    """sum over queries i of (position + 1), position = Lk - Lq + i."""
+    return B * (Lq * (Lk - Lq + 1) + Lq * (Lq - 1) // 2)
+
+
+def time_steps(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(s)
+    for _ in range(steps):
+        fn()
+    ev1.record(s)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps  # ms per step
+
+
+def headline(args, torch, sa, inputs):
+    wl = inputs.WORKLOADS["prefill_64k"]
+    dev = torch.device("cuda:0")
+    q, k, w = inputs.indexer_inputs(wl, 0, dev)
+    t_cache = torch.empty(wl.B, wl.Lq, wl.topk, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        sa.idx_cache_route("F", 0, q, k, w, t_cache)
+
+    ms = time_steps(step, args.steps, args.warmup, torch)
+    pairs = causal_pairs(wl.Lq, wl.Lk, wl.B)
+    flops = pairs * wl.H * wl.D * 2
+    return wl, ms, pairs, flops
+
+
+def decode(args, torch, sa, inputs):
+    wl = inputs.WORKLOADS["decode_200k"]
+    dev = torch.device("cuda:0")
+    q, k, w = inputs.indexer_inputs(wl, 0, dev)
+    qa, kv = inputs.attention_inputs(wl, 0, dev)
+    t = torch.empty(wl.B, wl.Lq, wl.topk, dtype=torch.int32, device=dev)
+    out = torch.empty(wl.B, wl.Lq, wl.Hq, wl.Dv, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(sa.idx_score_topk_workspace(q, k, w, wl.topk), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)   # evicts the 256 MB MALL
+    scale = 1.0 / math.sqrt(wl.Dqk)
+    sa.idx_cache_route("FSSS", 0, q, k, w, t, ws=ws)
+    torch.cuda.synchronize()
+    n = max(3, args.steps)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        tot = 0.0
+        for _ in range(n):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        return tot / n
+
+    t_idx = timed(lambda: sa.idx_cache_route("FSSS", 0, q, k, w, t, ws=ws))
+    t_att = timed(lambda: sa.sparse_mla_attn(qa, kv, t, scale, wl.Dv, out=out))
+    t_f = t_idx + t_att
+    gathered = wl.B * wl.Lq * wl.topk * wl.Dqk * 2
+    key_bytes = wl.B * wl.Lk * wl.D
+    tok = wl.B * wl.Lq
+    return {
+        "workload": "decode_200k", "batch": wl.B, "context": wl.Lk,
+        "indexer_topk_ms": round(t_idx, 4), "sparse_mla_ms": round(t_att, 4),
+        "full_layer_tok_s": round(tok / (t_f * 1e-3), 1),
+        "shared_layer_tok_s": round(tok / (t_att * 1e-3), 1),
+        "group_FSSS_tok_s": round(tok / ((t_f + 3 * t_att) * 1e-3), 1),
+        "group_FFFF_tok_s": round(tok / (4 * t_f * 1e-3), 1),
+        "indexer_key_read_GBs": round(key_bytes / (t_idx * 1e-3) / 1e9, 1),
+        "gather_GBs": round(gathered / (t_att * 1e-3) / 1e9, 1),
+        "gather_frac_hbm": round(gathered / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "note": "caches flushed before each timed call; one layer = one call each",
+    }
+
+
+def cpu_baseline(args, inputs, torch):
+    """Oracle rows/s on the host, scaled to pairs/s (bounded seeded row sample)."""
+    import numpy as np
+
+    import oracle
+    wl = inputs.WORKLOADS["prefill_64k"]
+    q, k, w = inputs.indexer_inputs(wl, 0, "cuda:0")
+    qr = q.cpu().view(torch.uint8).numpy()
+    kr = k.cpu().view(torch.uint8).numpy()
+    wr = w.cpu().view(torch.int16).numpy()
+    del q, k, w
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(2024)
+    order = rng.permutation(wl.Lq)
+    done_rows, done_pairs, wall = 0, 0, 0.0
+    batch = 2 * threads
+    while wall < args.cpu_seconds and done_rows < wl.Lq:
+        rows = np.sort(order[done_rows:done_rows + batch]).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.indexer_topk(qr, kr, wr, ("fp8", "fp8", "bf16"), wl.topk, rows=rows, nthreads=threads)
+        wall += time.perf_counter() - t0
+        done_rows += rows.size
+        done_pairs += int((rows + 1).sum())
+    return {"value": round(done_pairs / wall, 1), "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_rows} seeded random query rows of prefill_64k ({done_pairs} causal pairs, "
+                      f"fp64 scores + top-k), {wall:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    import sparse_attention_indexer_lightning_amd as sa
+    from sparse_attention_indexer_lightning_amd import inputs
+
+    sa.lib()
+    wl, ms, pairs, flops = headline(args, torch, sa, inputs)
+    if args.profile_only:
+        print(json.dumps({"ms_per_step": ms}))
+        return
+    achieved = flops / (ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("kernel_source_sha") == _kernel_sha():
+            traffic = rec.get("bytes_per_launch")
+    line = {
+        "metric": "indexer+top-k scored (q,key) pairs/s at L=64K; 200K-ctx sparse decode tok/s",
+        "value": round(pairs / (ms * 1e-3), 1),
+        "unit": "pairs/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8", "data": "synthetic",
+        "config": {"workload": "prefill_64k", "B": wl.B, "L": wl.Lq, "H_I": wl.H, "d_I": wl.D,
+                   "topk": wl.topk, "q_k": "fp8_e4m3", "w": "bf16", "pairs_per_step": pairs,
+                   "step": "idx_cache_route on a Full layer (fused score + top-k, T written)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "prefill_kernel<FP8,128,64,u16>",
+                     "flops_per_launch": flops},
+    }
+    if not args.no_decode:
+        line["secondary"] = decode(args, torch, sa, inputs)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, inputs, torch)
+    print(json.dumps(line))
+
+
+def _kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in ("indexer.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "sparse_attention_indexer_lightning_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()
