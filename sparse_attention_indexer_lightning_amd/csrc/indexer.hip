@@ -4,30 +4,41 @@
 // Attention um 75% reduziert", section "Wie der Indexer funktioniert und warum
 // MLA entscheidend ist"; parapluman.nl, section "Het DSA-knelpunt"):
 //     I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]),   s <= position(t)
-// followed by the top-k of each row (same page, section "Einfache
-// Implementierung, enorme Effizienzgewinne").
+// followed by the top-k of each row (same itoverdose.com page, section
+// "Einfache Implementierung, enorme Effizienzgewinne").
 //
 // Prefill kernel (many queries per sequence).  One workgroup owns R
 // consecutive query rows of one sequence and sweeps that sequence's keys in
-// blocks of 64, staging each key block in LDS.  Each wavefront holds its rows'
-// queries as MFMA A-fragments (64 (row, head) pairs = four 16-row fragments)
-// in registers for the whole sweep; per 16-key sub-block it issues four MFMAs
-// (fp8 16x16x128, or bf16 16x16x32 per 32-wide slice of d).  The ReLU and the
-// head-weighted sum run on the fp32 accumulators in registers; the head sum
-// finishes with a two-step cross-lane transpose-reduce that leaves lane l
-// holding the score of key (block + l).  Scores never reach HBM.
+// blocks of 64, staging each key block in LDS (double-buffered through
+// registers).  Each wavefront holds its rows' queries as MFMA A-fragments
+// (64 (row, head) pairs = four 16-row fragments) in registers for the whole
+// sweep.  Per 16-key sub-block it issues four MFMAs (fp8 16x16x128, or bf16
+// 16x16x32 per 32-wide slice of d); the MFMAs of sub-block j+1 are interleaved
+// with the ReLU / head-weight epilogue of sub-block j.  The head sum finishes
+// with a cross-lane transpose-reduce on v_permlane32_swap / v_permlane16_swap
+// that leaves lane l holding the score of key (block + l).  Scores never
+// reach HBM.
 //
 // Streaming top-k.  Each row owns an LDS candidate buffer of `cap` entries
-// (order-preserving 32-bit score key + key index) and a threshold key.  A key
-// enters the buffer when its key is strictly above the threshold; appends go
+// (order-preserving 32-bit score key + key index) and a threshold key; a key
+// enters the buffer when its key is strictly above the threshold.  Appends go
 // in ascending key order (ballot + prefix count), so the buffer stays sorted
-// by index.  When the buffer cannot take another block, the owning wavefront
-// finds the exact k-th largest key by MSB-first radix select (8-bit digits,
-// LDS histogram) and keeps, in place and in order, every entry above it plus
-// the lowest-index entries equal to it, then raises the threshold to it.
-// Keys equal to the threshold that arrive later have larger indices and can
-// never displace a kept entry, so strict ">" is exact.  At the end one more
-// selection leaves exactly min(k, p+1) entries, already in ascending order.
+// by index.  Two ways to shrink a full buffer:
+//  * exact: MSB-first radix select (8-bit digits, LDS histogram) finds the
+//    k-th largest key; a stable in-place filter keeps every entry above it
+//    plus the lowest-index entries equal to it, and it becomes the threshold
+//    (a later key equal to it has a larger index and can never win, so ">"
+//    is exact);
+//  * binned (one query row per wavefront): every appended key also bumps a
+//    256-bin histogram over a window [lo, lo + 256 << shift) of key space;
+//    the bin holding the k-th largest key is read off the histogram, and the
+//    filter keeps every entry at or above that bin's lower edge (at least k
+//    entries, all of them better than anything dropped), which then bounds
+//    the threshold.  Falls back to the exact path when it frees too little.
+// With one row per wavefront, compactions are batched at the block barrier:
+// when any row must compact, every row past half its slack compacts too, so
+// waves stall on each other's compactions far less often.  At the end the
+// exact selection leaves min(k, p+1) entries, already in ascending order.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -92,27 +103,34 @@ __device__ __forceinline__ float load_w(const void *w, Enc enc, size_t idx) {
     return reinterpret_cast<const float *>(w)[idx];
 }
 
-// Lane group g holds partial sums p[j] of sub-block j for the same 16 keys as
-// the other three groups; returns the full sum of sub-block g.
-__device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2, float p3, int g) {
-    const bool lo = g < 2;
-    float ka = lo ? p0 : p2, kb = lo ? p1 : p3;
-    const float sa = lo ? p2 : p0, sb = lo ? p3 : p1;
-    ka += shfl_xor(sa, 32);
-    kb += shfl_xor(sb, 32);
-    const bool odd = (g & 1) != 0;
-    const float keep = odd ? kb : ka, send = odd ? ka : kb;
-    return keep + shfl_xor(send, 16);
+// Lane group g (lanes 16g..16g+15) holds partial sums p[j] of sub-block j for
+// the same 16 keys as the other three groups; returns the full sum of
+// sub-block g.  permlane32_swap(x, y) exchanges the upper half of x with the
+// lower half of y, permlane16_swap(x, y) the odd 16-lane rows of x with the
+// even rows of y; in both cases x' + y' is, per lane, the sum of the value it
+// keeps and its partner's copy of the same sub-block.
+__device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2, float p3) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+    const float a = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // sub-block 0 (lanes 0-31) / 2
+    const float b = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // sub-block 1 / 3
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
 }
 
 // ---------------------------------------------------------------- selection
 
-// Exact k-th largest key among buf_key[0..cnt) (cnt >= k), then in-place
-// stable compaction to the k best (ties: lowest index = earliest entry).
-// Wave-level; `hist` is this wave's 256-entry LDS scratch.
+// Exact k-th largest key among bkey[0..cnt) (cnt >= k), then in-place stable
+// compaction to the k best (ties: lowest index = earliest entry).  Wave-level;
+// `hist` is this wave's 256-entry LDS scratch.  Returns the k-th largest key.
 template <typename IdxT>
-__device__ void select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, uint32_t &thr, int k, uint32_t *hist,
-                               int lane) {
+__device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, uint32_t *hist, int lane) {
     uint32_t prefix = 0, pmask = 0;
     int need = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -179,7 +197,119 @@ __device__ void select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, uint32_t &t
         eqseen += __popcll(em);
     }
     cnt = out;
-    thr = prefix;
+    return prefix;
+}
+
+// Binned-selection state of one row (wave-uniform, one row per wavefront).
+struct BinState {
+    int cnt;          // entries in the buffer
+    uint32_t thr;     // append filter: key > thr
+    uint32_t lo;      // histogram window base (<= every buffered key)
+    int shift;        // bin width 2^shift in key units
+    uint32_t maxkey;  // largest key ever appended
+    bool hist_ok;     // histogram describes the buffer
+};
+
+__device__ __forceinline__ uint32_t bin_of(uint32_t key, uint32_t lo, int shift) {
+    const uint32_t b = (key - lo) >> shift;
+    return b < 255u ? b : 255u;
+}
+
+__device__ __forceinline__ int window_shift(uint32_t maxkey, uint32_t lo) {
+    const uint32_t span = maxkey > lo ? maxkey - lo : 0u;
+    const int bits = span ? 32 - __builtin_clz(span) : 0;
+    return bits > 8 ? bits - 8 : 0;
+}
+
+// Rebuild the histogram of bkey[0..cnt) for window (st.lo, st.shift).
+__device__ void rebuild_hist(const uint32_t *bkey, const BinState &st, uint32_t *hist, int lane) {
+    for (int j = lane; j < 256; j += kWave) hist[j] = 0;
+    wave_lds_sync();
+    for (int i = lane; i < st.cnt; i += kWave) atomicAdd(&hist[bin_of(bkey[i], st.lo, st.shift)], 1u);
+    wave_lds_sync();
+}
+
+template <typename IdxT>
+__device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
+                              int lane) {
+    const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane);
+    st.thr = theta;
+    st.lo = theta;
+    st.shift = window_shift(st.maxkey, st.lo);
+    rebuild_hist(bkey, st, hist, lane);
+    st.hist_ok = true;
+}
+
+// Shrink the buffer using the histogram; exact selection when that frees too
+// little room.  Precondition: st.cnt >= k.
+template <typename IdxT>
+__device__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
+                               int lane) {
+    if (!st.hist_ok) {
+        compact_exact<IdxT>(bkey, bidx, st, k, cap, hist, lane);
+        return;
+    }
+    // bin b* holding the k-th largest key; `above` = entries in higher bins
+    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+    const uint32_t s = h0 + h1 + h2 + h3;
+    uint32_t S = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_down(S, o, kWave);
+        if (lane + o < kWave) S += v;
+    }
+    const uint32_t E = S - s;
+    const bool here = (E < (uint32_t)k) && (S >= (uint32_t)k);
+    int bsel;
+    uint32_t kept;
+    {
+        uint32_t c = E;
+        if (c + h3 >= (uint32_t)k) { bsel = 3; kept = c + h3; }
+        else {
+            c += h3;
+            if (c + h2 >= (uint32_t)k) { bsel = 2; kept = c + h2; }
+            else {
+                c += h2;
+                if (c + h1 >= (uint32_t)k) { bsel = 1; kept = c + h1; }
+                else { c += h1; bsel = 0; kept = c + h0; }
+            }
+        }
+    }
+    const uint64_t m = ballot(here);
+    const int src = m ? __builtin_ctzll(m) : 0;
+    const int bstar = __shfl(4 * lane + bsel, src, kWave);
+    const uint32_t nkeep = __shfl(kept, src, kWave);
+    if (!m || bstar == 0 || bstar == 255 || (int)nkeep > cap - 2 * KB) {
+        compact_exact<IdxT>(bkey, bidx, st, k, cap, hist, lane);
+        return;
+    }
+    const uint32_t edge = st.lo + ((uint32_t)bstar << st.shift);   // keep keys >= edge
+    const uint32_t new_lo = edge;
+    const int new_shift = window_shift(st.maxkey, new_lo);
+    for (int j = lane; j < 256; j += kWave) hist[j] = 0;
+    wave_lds_sync();
+    int out = 0;
+    for (int base = 0; base < st.cnt; base += kWave) {
+        const int i = base + lane;
+        uint32_t u = 0;
+        IdxT ix = 0;
+        if (i < st.cnt) { u = bkey[i]; ix = bidx[i]; }
+        const bool keep = i < st.cnt && u >= edge;
+        const uint64_t km = ballot(keep);
+        const int pos = out + lanes_below(km);
+        wave_lds_sync();
+        if (keep) {
+            bkey[pos] = u;
+            bidx[pos] = ix;
+            atomicAdd(&hist[bin_of(u, new_lo, new_shift)], 1u);
+        }
+        wave_lds_sync();
+        out += __popcll(km);
+    }
+    st.cnt = out;
+    st.thr = max(st.thr, edge - 1u);
+    st.lo = new_lo;
+    st.shift = new_shift;
 }
 
 struct PrefillParams {
@@ -193,7 +323,7 @@ struct PrefillParams {
 
 // LDS plan of the prefill kernel; identical on host and device.
 struct PrefillLds {
-    size_t ktile, stage, hist, state, bkey, bidx, total;
+    size_t ktile, stage, hist, flags, state, bkey, bidx, total;
 };
 
 __host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, int cap, int idx_bytes, bool staged) {
@@ -205,6 +335,8 @@ __host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, 
     off += staged ? (size_t)waves * tw * KB * 4 : 0;
     L.hist = off;
     off += (size_t)waves * 256 * 4;
+    L.flags = off;
+    off += 64;
     L.state = off;
     off += (size_t)R * 8;
     L.bkey = off;
@@ -217,10 +349,11 @@ __host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, 
 }
 
 template <Enc E, int D, int H, typename IdxT>
-__global__ __launch_bounds__(kMaxThreads) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillParams p) {
     using S = Shape<E, D>;
     constexpr int TW = 64 / H;              // query rows per wave
     constexpr bool kStaged = H < 16;        // scores go through LDS before selection
+    constexpr bool kBinned = TW == 1;       // binned selection + batched compaction
     const int waves = blockDim.x / kWave;
     const int R = waves * TW;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4, n = lane & 15;
@@ -230,6 +363,7 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(PrefillParams p) {
     unsigned char *ktile = smem + L.ktile;
     float *stage = reinterpret_cast<float *>(smem + L.stage) + (size_t)wave * TW * KB;
     uint32_t *hist = reinterpret_cast<uint32_t *>(smem + L.hist) + wave * 256;
+    int *flags = reinterpret_cast<int *>(smem + L.flags);
     int *rcnt = reinterpret_cast<int *>(smem + L.state);
     uint32_t *rthr = reinterpret_cast<uint32_t *>(smem + L.state) + R;
     uint32_t *bkey_all = reinterpret_cast<uint32_t *>(smem + L.bkey);
@@ -268,6 +402,9 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(PrefillParams p) {
         rcnt[wave * TW + t] = 0;
         rthr[wave * TW + t] = 0u;
     }
+    BinState st;
+    st.cnt = 0; st.thr = 0u; st.lo = 0u; st.shift = 0; st.maxkey = 0u; st.hist_ok = false;
+    const int want_level = p.topk + (p.cap - p.topk) / 2;
 
     // stage key block 0
     const int nchunk = KB * S::ROWB / 16;
@@ -301,21 +438,19 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(PrefillParams p) {
     // last position among this wave's valid rows (for skipping blocks)
     const int wlast = min(i0 + wave * TW + TW, p.Lq) - 1;
     const int wpmax = off + wlast;
+    const bool wave_has_rows = wlast >= i0 + wave * TW;
 
     for (int blk = 0; blk < nblk; ++blk) {
         const int cur = blk & 1;
         if (blk + 1 < nblk) fetch(blk + 1);
         const int base = blk * KB;
-        if (wlast >= i0 + wave * TW && base <= wpmax) {
+        bool need = false;
+        if (wave_has_rows && base <= wpmax) {
             const unsigned char *kt = ktile + (size_t)cur * KB * S::PITCH;
+            Frag<E, D> Bf[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) load_frag<E, D>(Bf[j], kt + (16 * j + n) * S::PITCH, g);
             v4f acc[4][4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                Frag<E, D> Bf;
-                load_frag<E, D>(Bf, kt + (16 * j + n) * S::PITCH, g);
-#pragma unroll
-                for (int f = 0; f < 4; ++f) acc[j][f] = frag_mma<E, D>(A[f], Bf);
-            }
             float sc[TW];
             if constexpr (!kStaged) {
                 // rows of fragment f all belong to query t = f * 16 / H
@@ -325,18 +460,35 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) part[t][j] = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int f = 0; f < 4; ++f) acc[0][f] = frag_mma<E, D>(A[f], Bf[0]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (j + 1 < 4) {
+#pragma unroll
+                        for (int f = 0; f < 4; ++f) acc[j + 1][f] = frag_mma<E, D>(A[f], Bf[j + 1]);
+                    }
 #pragma unroll
                     for (int f = 0; f < 4; ++f) {
                         const int t = (16 * f) / H;
 #pragma unroll
-                        for (int ii = 0; ii < 4; ++ii)
-                            part[t][j] += wv[f][ii] * fmaxf(acc[j][f][ii], 0.f);
+                        for (int ii = 0; ii < 4; ++ii) part[t][j] += wv[f][ii] * fmaxf(acc[j][f][ii], 0.f);
                     }
+                    if (j + 1 < 4) {
+                        // interleave the next sub-block's MFMAs with this epilogue
 #pragma unroll
-                for (int t = 0; t < TW; ++t)
-                    sc[t] = transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3], g);
+                        for (int f = 0; f < 4; ++f) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < TW; ++t) sc[t] = transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3]);
             } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int f = 0; f < 4; ++f) acc[j][f] = frag_mma<E, D>(A[f], Bf[j]);
                 // H = 4: lane group g holds all heads of query 4f+g;
                 // H = 8: groups g and g^1 hold the two halves of query 2f+g/2.
 #pragma unroll
@@ -358,36 +510,74 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(PrefillParams p) {
                 for (int t = 0; t < TW; ++t) sc[t] = stage[t * KB + lane];
                 wave_lds_sync();
             }
-            // selection, one row at a time
-#pragma unroll
-            for (int t = 0; t < TW; ++t) {
-                const int i = i0 + wave * TW + t;
-                if (i >= p.Lq) continue;
+
+            // selection
+            if constexpr (kBinned) {
+                const int i = i0 + wave;
                 const int pos = off + i;
-                if (base > pos) continue;
-                const int s = base + lane;
-                const int row = wave * TW + t;
-                if (p.scores && s < p.Lk)
-                    p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc[t] : -INFINITY;
-                int cnt = rcnt[row];
-                uint32_t thr = rthr[row];
-                const uint32_t key = score_key(sc[t]);
-                const bool cand = s <= pos && key > thr;
-                const uint64_t m = ballot(cand);
-                if (m) {
-                    uint32_t *bk = bkey_all + (size_t)row * p.cap;
-                    IdxT *bi = bidx_all + (size_t)row * p.cap;
-                    const int at = cnt + lanes_below(m);
-                    if (cand) { bk[at] = key; bi[at] = (IdxT)s; }
-                    cnt += __popcll(m);
-                    wave_lds_sync();
-                    if (cnt > p.cap - KB) select_compact<IdxT>(bk, bi, cnt, thr, p.topk, hist, lane);
-                    if (lane == 0) { rcnt[row] = cnt; rthr[row] = thr; }
-                    wave_lds_sync();
+                if (i < p.Lq && base <= pos) {
+                    const int s = base + lane;
+                    if (p.scores && s < p.Lk)
+                        p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc[0] : -INFINITY;
+                    const uint32_t key = score_key(sc[0]);
+                    const bool cand = s <= pos && key > st.thr;
+                    const uint64_t m = ballot(cand);
+                    if (m) {
+                        uint32_t *bk = bkey_all + (size_t)wave * p.cap;
+                        IdxT *bi = bidx_all + (size_t)wave * p.cap;
+                        const int at = st.cnt + lanes_below(m);
+                        if (cand) {
+                            bk[at] = key;
+                            bi[at] = (IdxT)s;
+                            if (st.hist_ok) atomicAdd(&hist[bin_of(key, st.lo, st.shift)], 1u);
+                        }
+                        st.cnt += __popcll(m);
+                        st.maxkey = max(st.maxkey, wave_max_u32(cand ? key : 0u));
+                    }
+                    need = st.cnt > p.cap - KB;
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < TW; ++t) {
+                    const int i = i0 + wave * TW + t;
+                    if (i >= p.Lq) continue;
+                    const int pos = off + i;
+                    if (base > pos) continue;
+                    const int s = base + lane;
+                    const int row = wave * TW + t;
+                    if (p.scores && s < p.Lk)
+                        p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc[t] : -INFINITY;
+                    int cnt = rcnt[row];
+                    uint32_t thr = rthr[row];
+                    const uint32_t key = score_key(sc[t]);
+                    const bool cand = s <= pos && key > thr;
+                    const uint64_t m = ballot(cand);
+                    if (m) {
+                        uint32_t *bk = bkey_all + (size_t)row * p.cap;
+                        IdxT *bi = bidx_all + (size_t)row * p.cap;
+                        const int at = cnt + lanes_below(m);
+                        if (cand) { bk[at] = key; bi[at] = (IdxT)s; }
+                        cnt += __popcll(m);
+                        wave_lds_sync();
+                        if (cnt > p.cap - KB) thr = select_compact<IdxT>(bk, bi, cnt, p.topk, hist, lane);
+                        if (lane == 0) { rcnt[row] = cnt; rthr[row] = thr; }
+                        wave_lds_sync();
+                    }
                 }
             }
         }
+        if constexpr (kBinned) {
+            if (lane == 0) flags[wave] = need ? 1 : 0;
+        }
         __syncthreads();
+        if constexpr (kBinned) {
+            int any = 0;
+            for (int w = 0; w < waves; ++w) any |= flags[w];
+            if (any && st.cnt > want_level) {
+                compact_binned<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, st, p.topk,
+                                     p.cap, hist, lane);
+            }
+        }
         if (blk + 1 < nblk) stash(cur ^ 1);
         __syncthreads();
     }
@@ -397,11 +587,10 @@ __global__ __launch_bounds__(kMaxThreads) void prefill_kernel(PrefillParams p) {
         const int i = i0 + wave * TW + t;
         if (i >= p.Lq) break;
         const int row = wave * TW + t;
-        int cnt = rcnt[row];
-        uint32_t thr = rthr[row];
+        int cnt = kBinned ? st.cnt : rcnt[row];
         uint32_t *bk = bkey_all + (size_t)row * p.cap;
         IdxT *bi = bidx_all + (size_t)row * p.cap;
-        if (cnt > p.topk) select_compact<IdxT>(bk, bi, cnt, thr, p.topk, hist, lane);
+        if (cnt > p.topk) (void)select_compact<IdxT>(bk, bi, cnt, p.topk, hist, lane);
         int32_t *o = p.t_out + ((size_t)b * p.Lq + i) * p.topk;
         for (int j = lane; j < p.topk; j += kWave) o[j] = j < cnt ? (int32_t)bi[j] : -1;
         if (p.scores) {
@@ -471,7 +660,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
                 for (int ii = 0; ii < 4; ++ii) part[j] += wv[f][ii] * fmaxf(a[ii], 0.f);
             }
         }
-        const float sc = transpose_reduce4(part[0], part[1], part[2], part[3], g);
+        const float sc = transpose_reduce4(part[0], part[1], part[2], part[3]);
         if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
     }
 }
@@ -515,18 +704,23 @@ PrefillPlan plan_prefill(const IndexerArgs &a) {
     int min_waves = (nchunk + kChunkMax * kWave - 1) / (kChunkMax * kWave);
     if (min_waves < 1) min_waves = 1;
     for (int waves = 8; waves >= min_waves; waves /= 2) {
-        // room beyond k: at least one block of appends (KB); more room means
-        // fewer re-selections per row.  Take the most LDS allows, up to 1024.
-        for (int slack = 1024; slack >= KB; slack /= 2) {
-            const int cap = a.topk + slack;
-            const PrefillLds L = prefill_lds(waves, tw, pitch, cap, pl.idx_bytes, staged);
-            if (L.total <= kLdsBudget) {
-                pl.waves = waves;
-                pl.cap = cap;
-                pl.lds = L.total;
-                pl.ok = true;
-                return pl;
-            }
+        // room beyond k: at least two blocks of appends; more room means fewer
+        // compactions per row.  Take the most LDS allows (multiple of 64, <= 2048).
+        const PrefillLds base = prefill_lds(waves, tw, pitch, 0, pl.idx_bytes, staged);
+        if (base.total + 64 > kLdsBudget) {
+            if (waves == 1) break;
+            continue;
+        }
+        const size_t per_entry = (size_t)waves * tw * (4 + pl.idx_bytes);
+        long cap = (long)((kLdsBudget - base.total - 32) / per_entry);
+        cap = (cap / KB) * KB;
+        if (cap > a.topk + 2048) cap = ((a.topk + 2048) / KB) * KB;
+        if (cap >= a.topk + 2 * KB) {
+            pl.waves = waves;
+            pl.cap = (int)cap;
+            pl.lds = prefill_lds(waves, tw, pitch, pl.cap, pl.idx_bytes, staged).total;
+            pl.ok = pl.lds <= kLdsBudget;
+            if (pl.ok) return pl;
         }
         if (waves == 1) break;
     }
