@@ -40,6 +40,11 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// max(x, 0) for fp32 as one integer max: every negative float (-0 included)
+// is a negative int32, every positive float a positive one.  Unlike fmaxf it
+// needs no NaN canonicalisation of MFMA results.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // D(16x16, fp32) = A(16x128, fp8 e4m3) * B(128x16, fp8 e4m3) + C.
 // Lane l supplies row/column l%16 and the 32 k-values 32*(l/16)..+31 of A/B;
 // it receives D[4*(l/16)+i][l%16], i = 0..3.

@@ -130,7 +130,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // compaction to the k best (ties: lowest index = earliest entry).  Wave-level;
 // `hist` is this wave's 256-entry LDS scratch.  Returns the k-th largest key.
 template <typename IdxT>
-__device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, uint32_t *hist, int lane) {
+__device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, uint32_t *hist, int lane,
+                                   uint32_t *kept_max = nullptr) {
     uint32_t prefix = 0, pmask = 0;
     int need = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -178,6 +179,7 @@ __device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, 
     wave_lds_sync();
     // keep: key > prefix, or key == prefix among the first `need` such entries
     int out = 0, eqseen = 0;
+    uint32_t mx = 0;
     for (int base = 0; base < cnt; base += kWave) {
         const int i = base + lane;
         uint32_t u = 0;
@@ -191,12 +193,13 @@ __device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, 
         const uint64_t km = ballot(keep);
         const int pos = out + lanes_below(km);
         wave_lds_sync();
-        if (keep) { bkey[pos] = u; bidx[pos] = ix; }
+        if (keep) { bkey[pos] = u; bidx[pos] = ix; mx = max(mx, u); }
         wave_lds_sync();
         out += __popcll(km);
         eqseen += __popcll(em);
     }
     cnt = out;
+    if (kept_max) *kept_max = wave_max_u32(mx);
     return prefix;
 }
 
@@ -206,7 +209,7 @@ struct BinState {
     uint32_t thr;     // append filter: key > thr
     uint32_t lo;      // histogram window base (<= every buffered key)
     int shift;        // bin width 2^shift in key units
-    uint32_t maxkey;  // largest key ever appended
+    uint32_t maxkey;  // largest key kept by the last compaction (sets the window)
     bool hist_ok;     // histogram describes the buffer
 };
 
@@ -232,7 +235,7 @@ __device__ void rebuild_hist(const uint32_t *bkey, const BinState &st, uint32_t 
 template <typename IdxT>
 __device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
                               int lane) {
-    const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane);
+    const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane, &st.maxkey);
     st.thr = theta;
     st.lo = theta;
     st.shift = window_shift(st.maxkey, st.lo);
@@ -284,11 +287,8 @@ __device__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, 
         return;
     }
     const uint32_t edge = st.lo + ((uint32_t)bstar << st.shift);   // keep keys >= edge
-    const uint32_t new_lo = edge;
-    const int new_shift = window_shift(st.maxkey, new_lo);
-    for (int j = lane; j < 256; j += kWave) hist[j] = 0;
-    wave_lds_sync();
     int out = 0;
+    uint32_t mx = 0;
     for (int base = 0; base < st.cnt; base += kWave) {
         const int i = base + lane;
         uint32_t u = 0;
@@ -301,15 +301,17 @@ __device__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, 
         if (keep) {
             bkey[pos] = u;
             bidx[pos] = ix;
-            atomicAdd(&hist[bin_of(u, new_lo, new_shift)], 1u);
+            mx = max(mx, u);
         }
         wave_lds_sync();
         out += __popcll(km);
     }
     st.cnt = out;
     st.thr = max(st.thr, edge - 1u);
-    st.lo = new_lo;
-    st.shift = new_shift;
+    st.maxkey = wave_max_u32(mx);
+    st.lo = edge;
+    st.shift = window_shift(st.maxkey, st.lo);
+    rebuild_hist(bkey, st, hist, lane);
 }
 
 struct PrefillParams {
@@ -406,29 +408,33 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     st.cnt = 0; st.thr = 0u; st.lo = 0u; st.shift = 0; st.maxkey = 0u; st.hist_ok = false;
     const int want_level = p.topk + (p.cap - p.topk) / 2;
 
-    // stage key block 0
-    const int nchunk = KB * S::ROWB / 16;
+    // stage key block 0.  Thread tid stages 16-byte chunks tid + c*blockDim
+    // (c < cpt).  Keys past Lk are clamped to the last key: their scores lie
+    // beyond every query's position and are never used.
+    constexpr int CPK = S::ROWB / 16;               // chunks per key
+    const int nchunk = KB * CPK;
+    const int cpt = (nchunk + (int)blockDim.x - 1) / (int)blockDim.x;
+    const unsigned char *kseq = p.k + (size_t)b * p.Lk * S::ROWB;
     v4i kreg[kChunkMax];
     auto fetch = [&](int blk) {
 #pragma unroll
         for (int c = 0; c < kChunkMax; ++c) {
-            const int ci = tid + c * (int)blockDim.x;
-            kreg[c] = v4i{0, 0, 0, 0};
-            if (ci < nchunk) {
-                const int key = blk * KB + ci / (S::ROWB / 16);
-                if (key < p.Lk)
-                    kreg[c] = *reinterpret_cast<const v4i *>(
-                        p.k + ((size_t)b * p.Lk + key) * S::ROWB + (ci % (S::ROWB / 16)) * 16);
+            if (c < cpt) {
+                const int ci = min(tid + c * (int)blockDim.x, nchunk - 1);
+                const int key = min(blk * KB + ci / CPK, p.Lk - 1);
+                kreg[c] = *reinterpret_cast<const v4i *>(kseq + (size_t)key * S::ROWB + (ci % CPK) * 16);
             }
         }
     };
     auto stash = [&](int buf) {
 #pragma unroll
         for (int c = 0; c < kChunkMax; ++c) {
-            const int ci = tid + c * (int)blockDim.x;
-            if (ci < nchunk)
-                *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + (ci / (S::ROWB / 16)) * S::PITCH +
-                                         (ci % (S::ROWB / 16)) * 16) = kreg[c];
+            if (c < cpt) {
+                const int ci = tid + c * (int)blockDim.x;
+                if (ci < nchunk)
+                    *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + (ci / CPK) * S::PITCH +
+                                             (ci % CPK) * 16) = kreg[c];
+            }
         }
     };
     fetch(0);
@@ -459,8 +465,13 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 for (int t = 0; t < TW; ++t)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) part[t][j] = 0.f;
+                // Software pipeline over the four sub-blocks: phase j issues the
+                // MFMAs of sub-block j+1 interleaved (1 MFMA : 8 VALU) with the
+                // epilogue of sub-block j, whose accumulators were produced a
+                // whole phase earlier, so no VALU waits on an MFMA in flight.
 #pragma unroll
                 for (int f = 0; f < 4; ++f) acc[0][f] = frag_mma<E, D>(A[f], Bf[0]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if (j + 1 < 4) {
@@ -471,16 +482,16 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                     for (int f = 0; f < 4; ++f) {
                         const int t = (16 * f) / H;
 #pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) part[t][j] += wv[f][ii] * fmaxf(acc[j][f][ii], 0.f);
+                        for (int ii = 0; ii < 4; ++ii) part[t][j] += wv[f][ii] * relu(acc[j][f][ii]);
                     }
                     if (j + 1 < 4) {
-                        // interleave the next sub-block's MFMAs with this epilogue
 #pragma unroll
                         for (int f = 0; f < 4; ++f) {
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                         }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
                 for (int t = 0; t < TW; ++t) sc[t] = transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3]);
@@ -497,7 +508,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                     for (int f = 0; f < 4; ++f) {
                         float s = 0.f;
 #pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) s += wv[f][ii] * fmaxf(acc[j][f][ii], 0.f);
+                        for (int ii = 0; ii < 4; ++ii) s += wv[f][ii] * relu(acc[j][f][ii]);
                         if constexpr (H == 8) {
                             s += shfl_xor(s, 16);
                             if ((g & 1) == 0) stage[(2 * f + (g >> 1)) * KB + 16 * j + n] = s;
@@ -532,7 +543,6 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                             if (st.hist_ok) atomicAdd(&hist[bin_of(key, st.lo, st.shift)], 1u);
                         }
                         st.cnt += __popcll(m);
-                        st.maxkey = max(st.maxkey, wave_max_u32(cand ? key : 0u));
                     }
                     need = st.cnt > p.cap - KB;
                 }
@@ -567,19 +577,20 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             }
         }
         if constexpr (kBinned) {
-            if (lane == 0) flags[wave] = need ? 1 : 0;
+            if (lane == 0) flags[(blk & 1) * 8 + wave] = need ? 1 : 0;
         }
+        // The idle buffer was last read in block blk-1, which every wave has
+        // left (barrier below); after this block's barrier it holds block blk+1.
+        if (blk + 1 < nblk) stash(cur ^ 1);
         __syncthreads();
         if constexpr (kBinned) {
             int any = 0;
-            for (int w = 0; w < waves; ++w) any |= flags[w];
+            for (int w = 0; w < waves; ++w) any |= flags[(blk & 1) * 8 + w];
             if (any && st.cnt > want_level) {
                 compact_binned<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, st, p.topk,
                                      p.cap, hist, lane);
             }
         }
-        if (blk + 1 < nblk) stash(cur ^ 1);
-        __syncthreads();
     }
 
     // final selection and output
@@ -657,7 +668,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
             for (int f = 0; f < 4; ++f) {
                 const v4f a = frag_mma<E, D>(A[f], Bf[j]);
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) part[j] += wv[f][ii] * fmaxf(a[ii], 0.f);
+                for (int ii = 0; ii < 4; ++ii) part[j] += wv[f][ii] * relu(a[ii]);
             }
         }
         const float sc = transpose_reduce4(part[0], part[1], part[2], part[3]);
