@@ -118,6 +118,18 @@ __device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2,
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// ReLU and head weights of one 16-key sub-block: the four fragments' rows are
+// summed as four independent chains, then added in fragment order.  Both the
+// fused and the split-key kernel use this, so they round identically.
+__device__ __forceinline__ void subblock_epilogue(const v4f (&acc)[4], const float (&wv)[4][4], float (&pf)[4]) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        pf[f] = wv[f][0] * relu(acc[f][0]);
+#pragma unroll
+        for (int ii = 1; ii < 4; ++ii) pf[f] += wv[f][ii] * relu(acc[f][ii]);
+    }
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
@@ -207,11 +219,21 @@ __device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, 
 struct BinState {
     int cnt;          // entries in the buffer
     uint32_t thr;     // append filter: key > thr
+    float thr_f;      // the same filter on scores: score > thr_f
     uint32_t lo;      // histogram window base (<= every buffered key)
     int shift;        // bin width 2^shift in key units
     uint32_t maxkey;  // largest key kept by the last compaction (sets the window)
     bool hist_ok;     // histogram describes the buffer
 };
+
+// Largest float whose order-preserving key is <= thr: for every finite f,
+// score_key(f) > thr  <=>  f > key_floor_float(thr).
+__device__ __forceinline__ float key_floor_float(uint32_t thr) {
+    if (thr >= 0x80000000u) return __uint_as_float(min(thr & 0x7FFFFFFFu, 0x7F800000u));
+    if (thr >= 0x7FFFFFFEu) return __uint_as_float(0x80000001u);   // -denorm_min
+    if (thr < 0x007FFFFFu) return -INFINITY;
+    return __uint_as_float(~thr);
+}
 
 __device__ __forceinline__ uint32_t bin_of(uint32_t key, uint32_t lo, int shift) {
     const uint32_t b = (key - lo) >> shift;
@@ -237,6 +259,7 @@ __device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, i
                               int lane) {
     const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane, &st.maxkey);
     st.thr = theta;
+    st.thr_f = key_floor_float(theta);
     st.lo = theta;
     st.shift = window_shift(st.maxkey, st.lo);
     rebuild_hist(bkey, st, hist, lane);
@@ -308,6 +331,7 @@ __device__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, 
     }
     st.cnt = out;
     st.thr = max(st.thr, edge - 1u);
+    st.thr_f = key_floor_float(st.thr);
     st.maxkey = wave_max_u32(mx);
     st.lo = edge;
     st.shift = window_shift(st.maxkey, st.lo);
@@ -320,6 +344,7 @@ struct PrefillParams {
     int32_t *t_out;
     float *scores;
     int B, Lq, Lk, topk, cap;
+    int nthreads;   // == blockDim.x, passed as an argument so it lives in an SGPR
     Enc w_enc;
 };
 
@@ -356,7 +381,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     constexpr int TW = 64 / H;              // query rows per wave
     constexpr bool kStaged = H < 16;        // scores go through LDS before selection
     constexpr bool kBinned = TW == 1;       // binned selection + batched compaction
-    const int waves = blockDim.x / kWave;
+    const int waves = p.nthreads / kWave;
     const int R = waves * TW;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4, n = lane & 15;
 
@@ -404,8 +429,9 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         rcnt[wave * TW + t] = 0;
         rthr[wave * TW + t] = 0u;
     }
+    if (tid < 3) flags[tid] = 0;
     BinState st;
-    st.cnt = 0; st.thr = 0u; st.lo = 0u; st.shift = 0; st.maxkey = 0u; st.hist_ok = false;
+    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u; st.shift = 0; st.maxkey = 0u; st.hist_ok = false;
     const int want_level = p.topk + (p.cap - p.topk) / 2;
 
     // stage key block 0.  Thread tid stages 16-byte chunks tid + c*blockDim
@@ -413,14 +439,14 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // beyond every query's position and are never used.
     constexpr int CPK = S::ROWB / 16;               // chunks per key
     const int nchunk = KB * CPK;
-    const int cpt = (nchunk + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int cpt = (nchunk + p.nthreads - 1) / p.nthreads;
     const unsigned char *kseq = p.k + (size_t)b * p.Lk * S::ROWB;
     v4i kreg[kChunkMax];
     auto fetch = [&](int blk) {
 #pragma unroll
         for (int c = 0; c < kChunkMax; ++c) {
             if (c < cpt) {
-                const int ci = min(tid + c * (int)blockDim.x, nchunk - 1);
+                const int ci = min(tid + c * p.nthreads, nchunk - 1);
                 const int key = min(blk * KB + ci / CPK, p.Lk - 1);
                 kreg[c] = *reinterpret_cast<const v4i *>(kseq + (size_t)key * S::ROWB + (ci % CPK) * 16);
             }
@@ -430,7 +456,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
         for (int c = 0; c < kChunkMax; ++c) {
             if (c < cpt) {
-                const int ci = tid + c * (int)blockDim.x;
+                const int ci = tid + c * p.nthreads;
                 if (ci < nchunk)
                     *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + (ci / CPK) * S::PITCH +
                                              (ci % CPK) * 16) = kreg[c];
@@ -439,6 +465,10 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     };
     fetch(0);
     stash(0);
+    // Every load issued so far (A fragments, head weights, block 0) has landed:
+    // inside the loop only the next block's staging loads are in flight, and
+    // the MFMAs never wait on them.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // last position among this wave's valid rows (for skipping blocks)
@@ -478,12 +508,10 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
                         for (int f = 0; f < 4; ++f) acc[j + 1][f] = frag_mma<E, D>(A[f], Bf[j + 1]);
                     }
+                    float pf[4];
+                    subblock_epilogue(acc[j], wv, pf);
 #pragma unroll
-                    for (int f = 0; f < 4; ++f) {
-                        const int t = (16 * f) / H;
-#pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) part[t][j] += wv[f][ii] * relu(acc[j][f][ii]);
-                    }
+                    for (int f = 0; f < 4; ++f) part[(16 * f) / H][j] += pf[f];
                     if (j + 1 < 4) {
 #pragma unroll
                         for (int f = 0; f < 4; ++f) {
@@ -530,14 +558,14 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                     const int s = base + lane;
                     if (p.scores && s < p.Lk)
                         p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc[0] : -INFINITY;
-                    const uint32_t key = score_key(sc[0]);
-                    const bool cand = s <= pos && key > st.thr;
+                    const bool cand = s <= pos && sc[0] > st.thr_f;
                     const uint64_t m = ballot(cand);
                     if (m) {
                         uint32_t *bk = bkey_all + (size_t)wave * p.cap;
                         IdxT *bi = bidx_all + (size_t)wave * p.cap;
                         const int at = st.cnt + lanes_below(m);
                         if (cand) {
+                            const uint32_t key = score_key(sc[0]);
                             bk[at] = key;
                             bi[at] = (IdxT)s;
                             if (st.hist_ok) atomicAdd(&hist[bin_of(key, st.lo, st.shift)], 1u);
@@ -577,16 +605,17 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             }
         }
         if constexpr (kBinned) {
-            if (lane == 0) flags[(blk & 1) * 8 + wave] = need ? 1 : 0;
+            // word blk%3 collects this block's requests; word (blk+1)%3 was last
+            // read before the previous barrier and is next written after this one
+            if (need && lane == 0) atomicOr(&flags[blk % 3], 1);
+            if (wave == 0 && lane == 0) flags[(blk + 1) % 3] = 0;
         }
         // The idle buffer was last read in block blk-1, which every wave has
         // left (barrier below); after this block's barrier it holds block blk+1.
         if (blk + 1 < nblk) stash(cur ^ 1);
         __syncthreads();
         if constexpr (kBinned) {
-            int any = 0;
-            for (int w = 0; w < waves; ++w) any |= flags[(blk & 1) * 8 + w];
-            if (any && st.cnt > want_level) {
+            if (flags[blk % 3] && st.cnt > want_level) {
                 compact_binned<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, st, p.topk,
                                      p.cap, hist, lane);
             }
@@ -663,13 +692,14 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
         float part[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            v4f a[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) a[f] = frag_mma<E, D>(A[f], Bf[j]);
+            float pf[4];
+            subblock_epilogue(a, wv, pf);
             part[j] = 0.f;
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const v4f a = frag_mma<E, D>(A[f], Bf[j]);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) part[j] += wv[f][ii] * relu(a[ii]);
-            }
+            for (int f = 0; f < 4; ++f) part[j] += pf[f];
         }
         const float sc = transpose_reduce4(part[0], part[1], part[2], part[3]);
         if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
@@ -689,6 +719,7 @@ hipError_t launch_prefill_t(const IndexerArgs &a, int waves, int cap, size_t lds
     p.t_out = a.t_out;
     p.scores = a.scores;
     p.B = a.B; p.Lq = a.Lq; p.Lk = a.Lk; p.topk = a.topk; p.cap = cap;
+    p.nthreads = waves * kWave;
     p.w_enc = a.w_enc;
     const int R = waves * (64 / H);
     const int nrb = (a.Lq + R - 1) / R;
