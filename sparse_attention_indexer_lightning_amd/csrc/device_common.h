@@ -52,6 +52,15 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i &a, const v8i &b, co
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// D(32x32, fp32) = A(32x64, fp8 e4m3) * B(64x32, fp8 e4m3) + C.
+// Lane l supplies row/column l%32 and the 32 k-values 32*(l/32)..+31 of A/B;
+// it receives D[8*(r/4) + 4*(l/32) + r%4][l%32] in register r = 0..15.
+__device__ __forceinline__ v16f mfma_fp8_32x32x64(const v8i &a, const v8i &b, const v16f &c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // D(16x16, fp32) = A(16x32, bf16) * B(32x16, bf16) + C.
 // Lane l supplies row/column l%16 and k-values 8*(l/16)..+7; output as above.
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf &a, const v8bf &b, const v4f &c) {

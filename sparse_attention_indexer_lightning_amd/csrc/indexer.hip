@@ -130,6 +130,83 @@ __device__ __forceinline__ void subblock_epilogue(const v4f (&acc)[4], const flo
     }
 }
 
+// ---- 64 heads x 64 keys on 32x32x64 fp8 MFMAs (one query per wavefront) ----
+// A fragments: row fragment rf (heads 32rf..32rf+31) and d-step s (d 64s..64s+63);
+// lane l holds head 32rf + l%32, d = 64s + 32(l/32) .. +31.
+struct Q32 {
+    v8i a[2][2];      // [rf][s]
+    float w[2][16];   // head weight of accumulator register r of row fragment rf
+};
+
+__device__ __forceinline__ v8i load32(const unsigned char *p) {
+    const v4i lo = *reinterpret_cast<const v4i *>(p);
+    const v4i hi = *reinterpret_cast<const v4i *>(p + 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// qrow: the query's 64 x 128 fp8 block; wrow(h): weight of head h.
+template <typename WF>
+__device__ __forceinline__ void load_q32(Q32 &Q, const unsigned char *qrow, WF wrow, int lane) {
+    const int m = lane & 31, hgrp = lane >> 5;
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) Q.a[rf][st] = load32(qrow + (32 * rf + m) * 128 + 64 * st + 32 * hgrp);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Q.w[rf][r] = wrow(32 * rf + 8 * (r / 4) + 4 * hgrp + (r % 4));
+    }
+}
+
+// Sum over the lane's 32 heads of w * relu(acc) for one 32-key column
+// fragment: four independent chains of eight, added pairwise.
+__device__ __forceinline__ float epi32(const v16f &a0, const v16f &a1, const Q32 &Q) {
+    float c[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        c[h] = Q.w[0][8 * h] * relu(a0[8 * h]);
+        c[2 + h] = Q.w[1][8 * h] * relu(a1[8 * h]);
+#pragma unroll
+        for (int r = 1; r < 8; ++r) {
+            c[h] += Q.w[0][8 * h + r] * relu(a0[8 * h + r]);
+            c[2 + h] += Q.w[1][8 * h + r] * relu(a1[8 * h + r]);
+        }
+    }
+    return (c[0] + c[1]) + (c[2] + c[3]);
+}
+
+// Scores of 64 keys for one query.  kb(cf, st) returns the lane's 32-byte B
+// piece: key 32cf + l%32, d = 64st + 32(l/32) .. +31.  Lane l gets key l.
+template <typename KB32>
+__device__ __forceinline__ float score64_mfma32(const Q32 &Q, KB32 kb) {
+    v8i B[2][2];
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) B[cf][st] = kb(cf, st);
+    const v16f z = {};
+    v16f acc[2][2];   // [rf][cf]
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) acc[rf][0] = mfma_fp8_32x32x64(Q.a[rf][0], B[0][0], z);
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) acc[rf][0] = mfma_fp8_32x32x64(Q.a[rf][1], B[0][1], acc[rf][0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) acc[rf][1] = mfma_fp8_32x32x64(Q.a[rf][0], B[1][0], z);
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) acc[rf][1] = mfma_fp8_32x32x64(Q.a[rf][1], B[1][1], acc[rf][1]);
+    const float p0 = epi32(acc[0][0], acc[1][0], Q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const float p1 = epi32(acc[0][1], acc[1][1], Q);
+    // lanes 0-31 hold column fragment 0 of their head half, lanes 32-63 the other half
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
@@ -405,11 +482,22 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int pmax = off + min(i0 + R, p.Lq) - 1;
     const int nblk = pmax / KB + 1;
 
+    constexpr bool kMfma32 = E == Enc::FP8 && H == 64 && D == 128;
+    Q32 Q32f;
+    if constexpr (kMfma32) {
+        const int i = i0 + wave;
+        if (i < p.Lq) {
+            const size_t qi = (size_t)b * p.Lq + i;
+            load_q32(Q32f, p.q + qi * H * S::ROWB, [&](int h) { return load_w(p.w, p.w_enc, qi * H + h); }, lane);
+        } else {
+            load_q32(Q32f, p.q, [&](int h) { return 0.f; }, lane);
+        }
+    }
     // A fragments: fragment f, row r = 16f + n -> (t, h) = (r / H, r % H)
     Frag<E, D> A[4];
     float wv[4][4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < 4 && !kMfma32; ++f) {
         const int r = 16 * f + n, t = r / H, h = r % H;
         const int i = i0 + wave * TW + t;
         if (i < p.Lq) {
@@ -483,12 +571,16 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         bool need = false;
         if (wave_has_rows && base <= wpmax) {
             const unsigned char *kt = ktile + (size_t)cur * KB * S::PITCH;
-            Frag<E, D> Bf[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) load_frag<E, D>(Bf[j], kt + (16 * j + n) * S::PITCH, g);
-            v4f acc[4][4];
             float sc[TW];
-            if constexpr (!kStaged) {
+            if constexpr (kMfma32) {
+                sc[0] = score64_mfma32(Q32f, [&](int cf, int st) {
+                    return load32(kt + (32 * cf + (lane & 31)) * S::PITCH + 64 * st + 32 * (lane >> 5));
+                });
+            } else if constexpr (!kStaged) {
+                Frag<E, D> Bf[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) load_frag<E, D>(Bf[j], kt + (16 * j + n) * S::PITCH, g);
+                v4f acc[4][4];
                 // rows of fragment f all belong to query t = f * 16 / H
                 float part[TW][4];
 #pragma unroll
@@ -524,6 +616,10 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
                 for (int t = 0; t < TW; ++t) sc[t] = transpose_reduce4(part[t][0], part[t][1], part[t][2], part[t][3]);
             } else {
+                Frag<E, D> Bf[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) load_frag<E, D>(Bf[j], kt + (16 * j + n) * S::PITCH, g);
+                v4f acc[4][4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -667,19 +763,34 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
     const int s1 = min(s0 + p.split, p.Lk);
     float *out = p.scores + (size_t)row * p.Lk;
 
+    constexpr bool kMfma32 = E == Enc::FP8 && D == 128;
     Frag<E, D> A[4];
     float wv[4][4];
+    Q32 Q32f;
+    if constexpr (kMfma32) {
+        load_q32(Q32f, p.q + (size_t)row * H * S::ROWB,
+                 [&](int h) { return load_w(p.w, p.w_enc, (size_t)row * H + h); }, lane);
+    } else {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        load_frag<E, D>(A[f], p.q + ((size_t)row * H + 16 * f + n) * S::ROWB, g);
+        for (int f = 0; f < 4; ++f) {
+            load_frag<E, D>(A[f], p.q + ((size_t)row * H + 16 * f + n) * S::ROWB, g);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) wv[f][ii] = load_w(p.w, p.w_enc, (size_t)row * H + 16 * f + 4 * g + ii);
+            for (int ii = 0; ii < 4; ++ii) wv[f][ii] = load_w(p.w, p.w_enc, (size_t)row * H + 16 * f + 4 * g + ii);
+        }
     }
     const unsigned char *kb = p.k + (size_t)b * p.Lk * S::ROWB;
     for (int base = s0 + wave * KB; base < s1; base += kDecodeWaves * KB) {
         const int s = base + lane;
         if (base > pos) {
             if (s < s1) out[s] = -INFINITY;
+            continue;
+        }
+        if constexpr (kMfma32) {
+            const float sc = score64_mfma32(Q32f, [&](int cf, int st) {
+                const int key = min(base + 32 * cf + (lane & 31), p.Lk - 1);
+                return load32(kb + (size_t)key * S::ROWB + 64 * st + 32 * (lane >> 5));
+            });
+            if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
             continue;
         }
         Frag<E, D> Bf[4];
