@@ -22,8 +22,12 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
-// Orders the LDS traffic of one wavefront: later LDS reads see earlier writes
-// by any lane of the same wavefront.
+// LDS instructions of one wavefront execute in issue order, so a later LDS
+// read sees an earlier LDS write by any lane of the same wavefront as long
+// as the compiler keeps program order; this is that compiler barrier.
+__device__ __forceinline__ void wave_lds_order() { __asm__ volatile("" ::: "memory"); }
+
+// Full wavefront-scope fence (waits for outstanding LDS operations).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

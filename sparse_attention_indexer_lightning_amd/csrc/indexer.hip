@@ -48,6 +48,8 @@ namespace {
 constexpr int KB = 64;          // keys per block (one per lane after the reduce)
 constexpr int kMaxThreads = 512;
 constexpr int kChunkMax = 4;    // 16-byte chunks each thread stages per key block
+constexpr int kPadEntries = 256; // candidate-buffer padding read by 4-per-lane passes
+constexpr int kHistWords = 320;  // 256 bins + one dummy slot per lane for masked-off updates
 
 template <Enc E, int D>
 struct Shape {
@@ -214,81 +216,169 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // ---------------------------------------------------------------- selection
+//
+// Candidate buffers are walked four consecutive entries per lane (256 per
+// wavefront step: one ds_read_b128 of keys, one ds_read_b64/b128 of indices),
+// so each pass over ~2.8K entries is 11 steps.  Buffers are padded by 256
+// entries so the last step may read past `cnt` without leaving LDS.
 
-// Exact k-th largest key among bkey[0..cnt) (cnt >= k), then in-place stable
-// compaction to the k best (ties: lowest index = earliest entry).  Wave-level;
-// `hist` is this wave's 256-entry LDS scratch.  Returns the k-th largest key.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+constexpr int kStep = 4 * kWave;   // entries per wavefront step
+static_assert(kStep == kPadEntries, "buffer padding must cover one wavefront step");
+
+template <typename IdxT>
+__device__ __forceinline__ void load4(const uint32_t *bk, const IdxT *bi, int e0, uint32_t (&k)[4], IdxT (&ix)[4]) {
+    const v4u kk = *reinterpret_cast<const v4u *>(bk + e0);
+    k[0] = kk[0]; k[1] = kk[1]; k[2] = kk[2]; k[3] = kk[3];
+    if constexpr (sizeof(IdxT) == 2) {
+        typedef unsigned short v4s __attribute__((ext_vector_type(4)));
+        const v4s ii = *reinterpret_cast<const v4s *>(bi + e0);
+        ix[0] = ii[0]; ix[1] = ii[1]; ix[2] = ii[2]; ix[3] = ii[3];
+    } else {
+        const v4u ii = *reinterpret_cast<const v4u *>(bi + e0);
+        ix[0] = ii[0]; ix[1] = ii[1]; ix[2] = ii[2]; ix[3] = ii[3];
+    }
+}
+
+// Bin b holding the need-th largest entry of a 256-bin histogram (bins in
+// ascending key order, lane l owns bins 4l..4l+3); `above` = entries in bins
+// above b.  Requires total >= need >= 1.
+__device__ __forceinline__ void hist_find(const uint32_t *hist, int need, int lane, int &bin, uint32_t &above) {
+    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+    const uint32_t s = h0 + h1 + h2 + h3;
+    uint32_t S = s;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t v = __shfl_down(S, o, kWave);
+        if (lane + o < kWave) S += v;
+    }
+    const uint32_t E = S - s;
+    const uint32_t nd = (uint32_t)need;
+    const bool here = E < nd && S >= nd;
+    int bsel;
+    uint32_t c = E;
+    if (c + h3 >= nd) bsel = 3;
+    else {
+        c += h3;
+        if (c + h2 >= nd) bsel = 2;
+        else {
+            c += h2;
+            if (c + h1 >= nd) bsel = 1;
+            else { c += h1; bsel = 0; }
+        }
+    }
+    const uint64_t m = ballot(here);
+    const int src = m ? __builtin_ctzll(m) : 0;
+    bin = __shfl(4 * lane + bsel, src, kWave);
+    above = __shfl(c, src, kWave);
+}
+
+// In-place stable filter of buf[0..cnt): keeps keys > gt_than, plus the
+// first `eq_keep` keys equal to eq_key (eq_keep = 0 disables).  Returns the
+// new count; *kept_max = largest kept key.
+template <typename IdxT>
+__device__ int filter4(uint32_t *bk, IdxT *bi, int cnt, uint32_t gt_than, uint32_t eq_key, int eq_keep, int lane,
+                       uint32_t *kept_max) {
+    int out = 0, eqseen = 0;
+    uint32_t mx = 0;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < cnt; base += kStep) {
+        const int e0 = base + 4 * lane;
+        uint32_t k[4];
+        IdxT ix[4];
+        load4(bk, bi, e0, k, ix);
+        bool eq[4], keep[4];
+        int eqb = 0, keepb = 0;
+        uint64_t EM[4], KM[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool valid = e0 + j < cnt;
+            eq[j] = valid && eq_keep > 0 && k[j] == eq_key;
+            EM[j] = ballot(eq[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) eqb += __popcll(EM[j] & lt);
+        int erank = eqseen + eqb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool valid = e0 + j < cnt;
+            keep[j] = valid && (k[j] > gt_than || (eq[j] && erank < eq_keep));
+            erank += eq[j] ? 1 : 0;
+            KM[j] = ballot(keep[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) keepb += __popcll(KM[j] & lt);
+        int pos = out + keepb;
+        // in-place: every write lands at or below an entry this step already read
+        wave_lds_order();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (keep[j]) {
+                bk[pos] = k[j];
+                bi[pos] = ix[j];
+                mx = max(mx, k[j]);
+                ++pos;
+            }
+        }
+        wave_lds_order();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            out += __popcll(KM[j]);
+            eqseen += __popcll(EM[j]);
+        }
+    }
+    if (kept_max) *kept_max = wave_max_u32(mx);
+    return out;
+}
+
+// Exact k-th largest key among bkey[0..cnt) (cnt >= k) by MSB-first radix
+// select, then in-place stable compaction to the k best (ties: lowest index =
+// earliest entry).  Wave-level; `hist` is this wave's 256-entry LDS scratch.
+// Returns the k-th largest key.
 template <typename IdxT>
 __device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, uint32_t *hist, int lane,
                                    uint32_t *kept_max = nullptr) {
-    uint32_t prefix = 0, pmask = 0;
-    int need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int j = lane; j < 256; j += kWave) hist[j] = 0;
-        wave_lds_sync();
-        for (int i = lane; i < cnt; i += kWave) {
-            const uint32_t u = bkey[i];
-            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-        }
-        wave_lds_sync();
-        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-                       h3 = hist[4 * lane + 3];
-        const uint32_t s = h0 + h1 + h2 + h3;
-        uint32_t S = s;  // inclusive suffix sum over lanes >= lane
+    // bits above `top` are common to every key (from the buffer's min and max)
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int base = 0; base < cnt; base += kStep) {
+        const int e0 = base + 4 * lane;
+        const v4u kk = *reinterpret_cast<const v4u *>(bkey + e0);
 #pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const uint32_t v = __shfl_down(S, o, kWave);
-            if (lane + o < kWave) S += v;
-        }
-        const uint32_t E = S - s;
-        const bool here = (E < (uint32_t)need) && (S >= (uint32_t)need);
-        int bsel;
-        uint32_t above;
-        {
-            uint32_t c = E;
-            if (c + h3 >= (uint32_t)need) { bsel = 3; above = c; }
-            else {
-                c += h3;
-                if (c + h2 >= (uint32_t)need) { bsel = 2; above = c; }
-                else {
-                    c += h2;
-                    if (c + h1 >= (uint32_t)need) { bsel = 1; above = c; }
-                    else { c += h1; bsel = 0; above = c; }
-                }
+        for (int j = 0; j < 4; ++j)
+            if (e0 + j < cnt) { mn = min(mn, kk[j]); mx = max(mx, kk[j]); }
+    }
+    mn = ~wave_max_u32(~mn);
+    mx = wave_max_u32(mx);
+    int top = (mn == mx) ? 0 : 32 - __builtin_clz(mn ^ mx);
+    uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
+    uint32_t prefix = mn & pmask;
+    int need = k;
+    while (top > 0) {
+        const int width = top < 8 ? top : 8;
+        const int shift = top - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int j = lane; j < kHistWords; j += kWave) hist[j] = 0;
+        wave_lds_order();
+        for (int base = 0; base < cnt; base += kStep) {
+            const int e0 = base + 4 * lane;
+            const v4u kk = *reinterpret_cast<const v4u *>(bkey + e0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool in = e0 + j < cnt && (kk[j] & pmask) == prefix;
+                atomicAdd(&hist[in ? ((kk[j] >> shift) & dmask) : 256u + lane], 1u);
             }
         }
-        const uint64_t m = ballot(here);
-        const int src = __builtin_ctzll(m);
-        const int bin = __shfl(4 * lane + bsel, src, kWave);
-        const uint32_t ab = __shfl(above, src, kWave);
+        wave_lds_order();
+        int bin;
+        uint32_t above;
+        hist_find(hist, need, lane, bin, above);
         prefix |= (uint32_t)bin << shift;
-        pmask |= 0xFFu << shift;
-        need -= (int)ab;
+        pmask |= dmask << shift;
+        need -= (int)above;
+        top = shift;
+        wave_lds_order();
     }
-    wave_lds_sync();
-    // keep: key > prefix, or key == prefix among the first `need` such entries
-    int out = 0, eqseen = 0;
-    uint32_t mx = 0;
-    for (int base = 0; base < cnt; base += kWave) {
-        const int i = base + lane;
-        uint32_t u = 0;
-        IdxT ix = 0;
-        if (i < cnt) { u = bkey[i]; ix = bidx[i]; }
-        const bool gt = i < cnt && u > prefix;
-        const bool eq = i < cnt && u == prefix;
-        const uint64_t em = ballot(eq);
-        const int erank = eqseen + lanes_below(em);
-        const bool keep = gt || (eq && erank < need);
-        const uint64_t km = ballot(keep);
-        const int pos = out + lanes_below(km);
-        wave_lds_sync();
-        if (keep) { bkey[pos] = u; bidx[pos] = ix; mx = max(mx, u); }
-        wave_lds_sync();
-        out += __popcll(km);
-        eqseen += __popcll(em);
-    }
-    cnt = out;
-    if (kept_max) *kept_max = wave_max_u32(mx);
+    cnt = filter4<IdxT>(bkey, bidx, cnt, prefix, prefix, need, lane, kept_max);
     return prefix;
 }
 
@@ -297,10 +387,9 @@ struct BinState {
     int cnt;          // entries in the buffer
     uint32_t thr;     // append filter: key > thr
     float thr_f;      // the same filter on scores: score > thr_f
-    uint32_t lo;      // histogram window base (<= every buffered key)
-    int shift;        // bin width 2^shift in key units
-    uint32_t maxkey;  // largest key kept by the last compaction (sets the window)
-    bool hist_ok;     // histogram describes the buffer
+    uint32_t maxkey;  // largest key kept by the last compaction
+    int shift;        // histogram bin width 2^shift (set from maxkey and thr)
+    bool binned;      // an exact selection has run (thr is a real threshold)
 };
 
 // Largest float whose order-preserving key is <= thr: for every finite f,
@@ -312,107 +401,59 @@ __device__ __forceinline__ float key_floor_float(uint32_t thr) {
     return __uint_as_float(~thr);
 }
 
-__device__ __forceinline__ uint32_t bin_of(uint32_t key, uint32_t lo, int shift) {
-    const uint32_t b = (key - lo) >> shift;
-    return b < 255u ? b : 255u;
-}
-
 __device__ __forceinline__ int window_shift(uint32_t maxkey, uint32_t lo) {
     const uint32_t span = maxkey > lo ? maxkey - lo : 0u;
     const int bits = span ? 32 - __builtin_clz(span) : 0;
     return bits > 8 ? bits - 8 : 0;
 }
 
-// Rebuild the histogram of bkey[0..cnt) for window (st.lo, st.shift).
-__device__ void rebuild_hist(const uint32_t *bkey, const BinState &st, uint32_t *hist, int lane) {
-    for (int j = lane; j < 256; j += kWave) hist[j] = 0;
-    wave_lds_sync();
-    for (int i = lane; i < st.cnt; i += kWave) atomicAdd(&hist[bin_of(bkey[i], st.lo, st.shift)], 1u);
-    wave_lds_sync();
-}
-
 template <typename IdxT>
-__device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
-                              int lane) {
+__device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, uint32_t *hist, int lane) {
     const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane, &st.maxkey);
     st.thr = theta;
     st.thr_f = key_floor_float(theta);
-    st.lo = theta;
-    st.shift = window_shift(st.maxkey, st.lo);
-    rebuild_hist(bkey, st, hist, lane);
-    st.hist_ok = true;
+    st.binned = true;
 }
 
-// Shrink the buffer using the histogram; exact selection when that frees too
-// little room.  Precondition: st.cnt >= k.
+// Shrink the buffer by binning: every buffered key is >= thr (keys equal to
+// it are ties kept by an exact selection), so bin keys over the window
+// [thr, thr + 256 << shift) (shift from the last kept maximum; larger keys
+// share the top bin), find the bin holding the k-th largest key and keep
+// every entry at or above that bin's lower edge: at least k entries, all
+// better than anything dropped.  Exact selection when this frees too little
+// room.  Precondition: st.cnt >= k.
 template <typename IdxT>
 __device__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
                                int lane) {
-    if (!st.hist_ok) {
-        compact_exact<IdxT>(bkey, bidx, st, k, cap, hist, lane);
+    if (!st.binned) {
+        compact_exact<IdxT>(bkey, bidx, st, k, hist, lane);
         return;
     }
-    // bin b* holding the k-th largest key; `above` = entries in higher bins
-    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const uint32_t s = h0 + h1 + h2 + h3;
-    uint32_t S = s;
+    const uint32_t lo = st.thr;
+    const int shift = window_shift(st.maxkey, lo);
+    for (int j = lane; j < kHistWords; j += kWave) hist[j] = 0;
+    wave_lds_order();
+    for (int base = 0; base < st.cnt; base += kStep) {
+        const int e0 = base + 4 * lane;
+        const v4u kk = *reinterpret_cast<const v4u *>(bkey + e0);
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t v = __shfl_down(S, o, kWave);
-        if (lane + o < kWave) S += v;
+        for (int j = 0; j < 4; ++j)
+            atomicAdd(&hist[e0 + j < st.cnt ? min((kk[j] - lo) >> shift, 255u) : 256u + lane], 1u);
     }
-    const uint32_t E = S - s;
-    const bool here = (E < (uint32_t)k) && (S >= (uint32_t)k);
-    int bsel;
-    uint32_t kept;
-    {
-        uint32_t c = E;
-        if (c + h3 >= (uint32_t)k) { bsel = 3; kept = c + h3; }
-        else {
-            c += h3;
-            if (c + h2 >= (uint32_t)k) { bsel = 2; kept = c + h2; }
-            else {
-                c += h2;
-                if (c + h1 >= (uint32_t)k) { bsel = 1; kept = c + h1; }
-                else { c += h1; bsel = 0; kept = c + h0; }
-            }
-        }
-    }
-    const uint64_t m = ballot(here);
-    const int src = m ? __builtin_ctzll(m) : 0;
-    const int bstar = __shfl(4 * lane + bsel, src, kWave);
-    const uint32_t nkeep = __shfl(kept, src, kWave);
-    if (!m || bstar == 0 || bstar == 255 || (int)nkeep > cap - 2 * KB) {
-        compact_exact<IdxT>(bkey, bidx, st, k, cap, hist, lane);
+    wave_lds_order();
+    int bstar;
+    uint32_t above;
+    hist_find(hist, k, lane, bstar, above);
+    const uint32_t nkeep = above + hist[bstar];
+    wave_lds_order();
+    if (bstar == 0 || bstar == 255 || (int)nkeep > cap - 2 * KB) {
+        compact_exact<IdxT>(bkey, bidx, st, k, hist, lane);
         return;
     }
-    const uint32_t edge = st.lo + ((uint32_t)bstar << st.shift);   // keep keys >= edge
-    int out = 0;
-    uint32_t mx = 0;
-    for (int base = 0; base < st.cnt; base += kWave) {
-        const int i = base + lane;
-        uint32_t u = 0;
-        IdxT ix = 0;
-        if (i < st.cnt) { u = bkey[i]; ix = bidx[i]; }
-        const bool keep = i < st.cnt && u >= edge;
-        const uint64_t km = ballot(keep);
-        const int pos = out + lanes_below(km);
-        wave_lds_sync();
-        if (keep) {
-            bkey[pos] = u;
-            bidx[pos] = ix;
-            mx = max(mx, u);
-        }
-        wave_lds_sync();
-        out += __popcll(km);
-    }
-    st.cnt = out;
-    st.thr = max(st.thr, edge - 1u);
+    const uint32_t edge = lo + ((uint32_t)bstar << shift);   // keep keys >= edge
+    st.cnt = filter4<IdxT>(bkey, bidx, st.cnt, edge - 1u, 0u, 0, lane, &st.maxkey);
+    st.thr = edge - 1u;
     st.thr_f = key_floor_float(st.thr);
-    st.maxkey = wave_max_u32(mx);
-    st.lo = edge;
-    st.shift = window_shift(st.maxkey, st.lo);
-    rebuild_hist(bkey, st, hist, lane);
 }
 
 struct PrefillParams {
@@ -438,16 +479,16 @@ __host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, 
     L.stage = off;
     off += staged ? (size_t)waves * tw * KB * 4 : 0;
     L.hist = off;
-    off += (size_t)waves * 256 * 4;
+    off += (size_t)waves * kHistWords * 4;
     L.flags = off;
     off += 64;
     L.state = off;
     off += (size_t)R * 8;
     L.bkey = off;
-    off += (size_t)R * cap * 4;
+    off += ((size_t)R * cap + kPadEntries) * 4;
     off = (off + 15) & ~(size_t)15;
     L.bidx = off;
-    off += (size_t)R * cap * idx_bytes;
+    off += ((size_t)R * cap + kPadEntries) * idx_bytes;
     L.total = (off + 15) & ~(size_t)15;
     return L;
 }
@@ -466,7 +507,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const PrefillLds L = prefill_lds(waves, TW, S::PITCH, p.cap, (int)sizeof(IdxT), kStaged);
     unsigned char *ktile = smem + L.ktile;
     float *stage = reinterpret_cast<float *>(smem + L.stage) + (size_t)wave * TW * KB;
-    uint32_t *hist = reinterpret_cast<uint32_t *>(smem + L.hist) + wave * 256;
+    uint32_t *hist = reinterpret_cast<uint32_t *>(smem + L.hist) + wave * kHistWords;
     int *flags = reinterpret_cast<int *>(smem + L.flags);
     int *rcnt = reinterpret_cast<int *>(smem + L.state);
     uint32_t *rthr = reinterpret_cast<uint32_t *>(smem + L.state) + R;
@@ -519,7 +560,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     if (tid < 3) flags[tid] = 0;
     BinState st;
-    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u; st.shift = 0; st.maxkey = 0u; st.hist_ok = false;
+    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.maxkey = 0u; st.shift = 0; st.binned = false;
     const int want_level = p.topk + (p.cap - p.topk) / 2;
 
     // stage key block 0.  Thread tid stages 16-byte chunks tid + c*blockDim
@@ -664,7 +705,6 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                             const uint32_t key = score_key(sc[0]);
                             bk[at] = key;
                             bi[at] = (IdxT)s;
-                            if (st.hist_ok) atomicAdd(&hist[bin_of(key, st.lo, st.shift)], 1u);
                         }
                         st.cnt += __popcll(m);
                     }
