@@ -5,13 +5,18 @@
 // "Einfache Implementierung, enorme Effizienzgewinne": T = top-k(I), with ties
 // going to the lower key index and T written in ascending index order.
 //
-// One workgroup (16 wavefronts) per row.  The k-th largest order-preserving key
-// is found by MSB-first radix select, four 8-bit digits, each digit one
-// coalesced pass over the row with a shared LDS histogram.  The output pass
-// walks the row in 1024-key chunks; one workgroup scan per chunk of the packed
-// pair (count above the threshold, count equal to it) gives every kept key its
-// output slot: slot = above_before + min(equal_before, equal_needed).  Keys
-// are therefore written in ascending order with no sort.
+// One workgroup (16 wavefronts) per row, on order-preserving 32-bit keys:
+//  1. bound: every thread keeps the 4 largest keys of its strided share of
+//     the row; the k-th largest of these 4096 keys is <= the row's k-th
+//     largest key (they are a subset of the row), so every member of the
+//     top-k is >= it;
+//  2. collect: one coalesced pass appends every key >= the bound to an LDS
+//     candidate list in ascending index order (block prefix sums);
+//  3. select: exact MSB-first radix select on the candidates, then one
+//     ordered pass writes the indices above the k-th key plus the lowest-index
+//     ties.
+// For i.i.d. scores the candidate list is a little over k long.  If it would
+// not fit in LDS, the row falls back to radix selection over the row in HBM.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -20,13 +25,132 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kLocal = 4;                  // keys kept per thread in step 1
+constexpr int kUnion = kThreads * kLocal;  // 4096
+constexpr int kCandCap = 8192;             // LDS candidate capacity
+constexpr int kDigit = 11;                 // radix digit width
+constexpr int kBins = 1 << kDigit;
+
+struct TopkShared {
+    uint32_t ukey[kUnion];          // step 1 union, then reused
+    uint32_t ckey[kCandCap];        // candidates: key
+    int32_t cidx[kCandCap];         //             index
+    uint32_t hist[kBins];
+    uint32_t wtot[2][kWaves];
+    int sh_bin;
+    uint32_t sh_above;
+};
+
+__device__ __forceinline__ uint32_t wave_max32(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
+}
+
+// The need-th largest key among `n` keys produced by get(i) (block-wide),
+// returning the key and, through *above, how many keys are strictly larger.
+// MSB-first radix select with 11-bit digits, starting below the bits that the
+// smallest and largest key share (so the first digit already spreads keys).
+template <typename Get>
+__device__ uint32_t block_select(TopkShared &sh, int n, int need, Get get, uint32_t *above_out) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int i = tid; i < n; i += kThreads) {
+        const uint32_t u = get(i);
+        mn = min(mn, u);
+        mx = max(mx, u);
+    }
+    mn = ~wave_max32(~mn);
+    mx = wave_max32(mx);
+    if (lane == 0) { sh.wtot[0][wave] = mn; sh.wtot[1][wave] = mx; }
+    __syncthreads();
+    mn = 0xFFFFFFFFu; mx = 0u;
+    for (int w = 0; w < kWaves; ++w) { mn = min(mn, sh.wtot[0][w]); mx = max(mx, sh.wtot[1][w]); }
+    int top = (mn == mx) ? 0 : 32 - __builtin_clz(mn ^ mx);
+    uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
+    uint32_t prefix = mn & pmask;
+    uint32_t above_total = 0;
+    while (top > 0) {
+        const int width = top < kDigit ? top : kDigit;
+        const int shift = top - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int j = tid; j < kBins; j += kThreads) sh.hist[j] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += kThreads) {
+            const uint32_t u = get(i);
+            if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        // suffix scan over kBins bins: lane l of wave 0 owns bins [32l, 32l+32)
+        if (wave == 0) {
+            uint32_t sum = 0;
+            for (int j = 0; j < kBins / kWave; ++j) sum += sh.hist[(kBins / kWave) * lane + j];
+            uint32_t S = sum;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t v = __shfl_down(S, o, kWave);
+                if (lane + o < kWave) S += v;
+            }
+            const uint32_t E = S - sum;
+            if (E < (uint32_t)need && S >= (uint32_t)need) {
+                uint32_t c = E;
+                int bsel = 0;
+                for (int j = kBins / kWave - 1; j >= 0; --j) {
+                    const uint32_t h = sh.hist[(kBins / kWave) * lane + j];
+                    if (c + h >= (uint32_t)need) { bsel = j; break; }
+                    c += h;
+                }
+                sh.sh_bin = (kBins / kWave) * lane + bsel;
+                sh.sh_above = c;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sh.sh_bin << shift;
+        pmask |= dmask << shift;
+        need -= (int)sh.sh_above;
+        above_total += sh.sh_above;
+        top = shift;
+        __syncthreads();
+    }
+    *above_out = above_total;
+    return prefix;
+}
+
+// Ordered output of the top-k from keys get(i), i < n, in index order:
+// slot = above_before + min(equal_before, need_eq), index = idx(i).
+template <typename Get, typename Idx>
+__device__ void ordered_output(TopkShared &sh, int n, uint32_t theta, int need_eq, int k, Get get, Idx idx,
+                               int32_t *out) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    uint32_t gt_base = 0, eq_base = 0;
+    int par = 0;
+    for (int c0 = 0; c0 < n; c0 += kThreads, par ^= 1) {
+        const int j = c0 + tid;
+        const uint32_t u = j < n ? get(j) : 0u;
+        const bool gt = j < n && u > theta;
+        const bool eq = j < n && u == theta;
+        const uint64_t gm = ballot(gt), em = ballot(eq);
+        if (lane == 0) sh.wtot[par][wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(em) << 16);
+        __syncthreads();
+        uint32_t before = 0, total = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t v = sh.wtot[par][w];
+            if (w < wave) before += v;
+            total += v;
+        }
+        const uint32_t gt_before = gt_base + (before & 0xFFFFu) + lanes_below(gm);
+        const uint32_t eq_before = eq_base + (before >> 16) + lanes_below(em);
+        const uint32_t ne = (uint32_t)need_eq;
+        if (gt || (eq && eq_before < ne)) out[gt_before + (eq_before < ne ? eq_before : ne)] = idx(j);
+        gt_base += total & 0xFFFFu;
+        eq_base += total >> 16;
+        if (gt_base + (eq_base < ne ? eq_base : ne) >= (uint32_t)k) break;
+    }
+}
 
 __global__ __launch_bounds__(kThreads) void row_topk_kernel(TopkArgs a) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t wtot[kWaves];
-    __shared__ int sh_bin;
-    __shared__ uint32_t sh_above;
-
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    TopkShared &sh = *reinterpret_cast<TopkShared *>(smem_raw);
     const int r = blockIdx.x;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     int pos;
@@ -42,86 +166,95 @@ __global__ __launch_bounds__(kThreads) void row_topk_kernel(TopkArgs a) {
     }
     const float *s = a.scores + (size_t)r * a.Lk;
 
-    uint32_t prefix = 0, pmask = 0;
-    int need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int j = tid; j < 256; j += kThreads) hist[j] = 0;
-        __syncthreads();
-        for (int j = tid; j < n; j += kThreads) {
-            const uint32_t u = score_key(s[j]);
-            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-                           h3 = hist[4 * lane + 3];
-            const uint32_t sum = h0 + h1 + h2 + h3;
-            uint32_t S = sum;
+    // 1. lower bound from the union of per-thread top-4 lists
+    uint32_t top[kLocal] = {0u, 0u, 0u, 0u};
+    for (int c0 = 0; c0 < n; c0 += 4 * kThreads) {
+        const int j0 = c0 + 4 * tid;
+        uint32_t u[4];
 #pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t v = __shfl_down(S, o, kWave);
-                if (lane + o < kWave) S += v;
-            }
-            const uint32_t E = S - sum;
-            if (E < (uint32_t)need && S >= (uint32_t)need) {
-                uint32_t c = E;
-                int bsel;
-                if (c + h3 >= (uint32_t)need) bsel = 3;
-                else {
-                    c += h3;
-                    if (c + h2 >= (uint32_t)need) bsel = 2;
-                    else {
-                        c += h2;
-                        if (c + h1 >= (uint32_t)need) bsel = 1;
-                        else { c += h1; bsel = 0; }
-                    }
-                }
-                sh_bin = 4 * lane + bsel;
-                sh_above = c;
+        for (int e = 0; e < 4; ++e) u[e] = j0 + e < n ? score_key(s[j0 + e]) : 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (u[e] > top[3]) {
+                top[3] = u[e];
+                if (top[3] > top[2]) { const uint32_t x = top[2]; top[2] = top[3]; top[3] = x; }
+                if (top[2] > top[1]) { const uint32_t x = top[1]; top[1] = top[2]; top[2] = x; }
+                if (top[1] > top[0]) { const uint32_t x = top[0]; top[0] = top[1]; top[1] = x; }
             }
         }
-        __syncthreads();
-        prefix |= (uint32_t)sh_bin << shift;
-        pmask |= 0xFFu << shift;
-        need -= (int)sh_above;
-        __syncthreads();
     }
+#pragma unroll
+    for (int i = 0; i < kLocal; ++i) sh.ukey[tid * kLocal + i] = top[i];
+    __syncthreads();
+    uint32_t dummy;
+    const uint32_t bound = block_select(sh, kUnion, k, [&](int i) { return sh.ukey[i]; }, &dummy);
 
-    // ordered output: slot = above_before + min(equal_before, need)
-    uint32_t gt_base = 0, eq_base = 0;
-    for (int c0 = 0; c0 < n; c0 += kThreads) {
-        const int j = c0 + tid;
-        uint32_t u = 0;
-        if (j < n) u = score_key(s[j]);
-        const bool gt = j < n && u > prefix;
-        const bool eq = j < n && u == prefix;
-        const uint64_t gm = ballot(gt), em = ballot(eq);
-        if (lane == 0) wtot[wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(em) << 16);
+    // 2. collect keys >= bound in index order (4 per thread per step)
+    uint32_t base = 0;
+    bool overflow = false;
+    int par = 0;
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int c0 = 0; c0 < n; c0 += 4 * kThreads, par ^= 1) {
+        const int j0 = c0 + 4 * tid;
+        uint32_t u[4];
+        bool f[4];
+        uint64_t B[4];
+        int below = 0, mine = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[e] = j0 + e < n ? score_key(s[j0 + e]) : 0u;
+            f[e] = j0 + e < n && u[e] >= bound;
+            B[e] = ballot(f[e]);
+            below += __popcll(B[e] & lt);
+            mine += __popcll(B[e]);
+        }
+        if (lane == 0) sh.wtot[par][wave] = (uint32_t)mine;
         __syncthreads();
-        uint32_t before = 0, total = 0;
+        uint32_t wbefore = 0, total = 0;
         for (int w = 0; w < kWaves; ++w) {
-            const uint32_t v = wtot[w];
-            if (w < wave) before += v;
+            const uint32_t v = sh.wtot[par][w];
+            if (w < wave) wbefore += v;
             total += v;
         }
-        const uint32_t gt_before = gt_base + (before & 0xFFFFu) + lanes_below(gm);
-        const uint32_t eq_before = eq_base + (before >> 16) + lanes_below(em);
-        if (gt || (eq && eq_before < (uint32_t)need)) {
-            const uint32_t slot = gt_before + (eq_before < (uint32_t)need ? eq_before : (uint32_t)need);
-            out[slot] = j;
+        uint32_t p = base + wbefore + (uint32_t)below;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (f[e]) {
+                if (p < (uint32_t)kCandCap) { sh.ckey[p] = u[e]; sh.cidx[p] = j0 + e; }
+                ++p;
+            }
         }
-        gt_base += total & 0xFFFFu;
-        eq_base += total >> 16;
-        __syncthreads();
-        if (gt_base + (eq_base < (uint32_t)need ? eq_base : (uint32_t)need) >= (uint32_t)k) break;
+        base += total;
+        if (base > (uint32_t)kCandCap) { overflow = true; break; }
     }
+    __syncthreads();
+
+    if (!overflow) {
+        // 3. exact selection among the candidates
+        const int nc = (int)base;
+        uint32_t above;
+        const uint32_t theta = block_select(sh, nc, k, [&](int i) { return sh.ckey[i]; }, &above);
+        const int need_eq = k - (int)above;
+        ordered_output(sh, nc, theta, need_eq, k, [&](int i) { return sh.ckey[i]; },
+                       [&](int i) { return sh.cidx[i]; }, out);
+        return;
+    }
+    // fallback: radix selection over the row in HBM
+    uint32_t above;
+    const uint32_t theta = block_select(sh, n, k, [&](int i) { return score_key(s[i]); }, &above);
+    ordered_output(sh, n, theta, k - (int)above, k, [&](int i) { return score_key(s[i]); },
+                   [&](int i) { return i; }, out);
 }
 
 }  // namespace
 
 hipError_t launch_row_topk(const TopkArgs &a, hipStream_t st) {
     if (a.R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(row_topk_kernel, dim3((unsigned)a.R), dim3(kThreads), 0, st, a);
+    const size_t lds = sizeof(TopkShared);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(row_topk_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(row_topk_kernel, dim3((unsigned)a.R), dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
 
