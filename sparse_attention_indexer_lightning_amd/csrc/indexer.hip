@@ -29,12 +29,13 @@
 //    plus the lowest-index entries equal to it, and it becomes the threshold
 //    (a later key equal to it has a larger index and can never win, so ">"
 //    is exact);
-//  * binned (one query row per wavefront): every appended key also bumps a
-//    256-bin histogram over a window [lo, lo + 256 << shift) of key space;
-//    the bin holding the k-th largest key is read off the histogram, and the
-//    filter keeps every entry at or above that bin's lower edge (at least k
-//    entries, all of them better than anything dropped), which then bounds
-//    the threshold.  Falls back to the exact path when it frees too little.
+//  * binned (one query row per wavefront): a 256-bin histogram of the
+//    buffered keys, log-spaced above a base key (finest just above it) and
+//    kept current by the appends, gives the bin holding the k-th largest key
+//    directly; the filter keeps every entry at or above that bin's lower edge
+//    (at least k entries, all of them better than anything dropped), which
+//    then bounds the threshold.  The histogram is rebuilt from the threshold
+//    when the cut's bin is too full; exact selection is the fallback.
 // With one row per wavefront, compactions are batched at the block barrier:
 // when any row must compact, every row past half its slack compacts too, so
 // waves stall on each other's compactions far less often.  At the end the
@@ -240,76 +241,98 @@ __device__ __forceinline__ void load4(const uint32_t *bk, const IdxT *bi, int e0
     }
 }
 
+// Inclusive prefix sum over the wavefront's lanes (lane l gets the sum over
+// lanes 0..l): Hillis-Steele shifts inside each 16-lane row, then the row
+// totals are carried across rows with the row-broadcast DPP forms.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return v;
+}
+
 // Bin b holding the need-th largest entry of a 256-bin histogram (bins in
-// ascending key order, lane l owns bins 4l..4l+3); `above` = entries in bins
-// above b.  Requires total >= need >= 1.
+// ascending key order); `above` = entries in bins above b.  Lane l looks at
+// bins 252-4l .. 255-4l, so a prefix sum over lanes counts from the top bin
+// down.  Requires total >= need >= 1.
 __device__ __forceinline__ void hist_find(const uint32_t *hist, int need, int lane, int &bin, uint32_t &above) {
-    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const uint32_t s = h0 + h1 + h2 + h3;
-    uint32_t S = s;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t v = __shfl_down(S, o, kWave);
-        if (lane + o < kWave) S += v;
-    }
-    const uint32_t E = S - s;
+    const int b0 = 4 * (kWave - 1 - lane);
+    const v4u hv = *reinterpret_cast<const v4u *>(hist + b0);
+    const uint32_t s = hv[0] + hv[1] + hv[2] + hv[3];
+    const uint32_t S = wave_incl_scan(s);   // entries in bins >= b0
+    const uint32_t E = S - s;               // entries in bins > b0 + 3
     const uint32_t nd = (uint32_t)need;
     const bool here = E < nd && S >= nd;
     int bsel;
     uint32_t c = E;
-    if (c + h3 >= nd) bsel = 3;
+    if (c + hv[3] >= nd) bsel = 3;
     else {
-        c += h3;
-        if (c + h2 >= nd) bsel = 2;
+        c += hv[3];
+        if (c + hv[2] >= nd) bsel = 2;
         else {
-            c += h2;
-            if (c + h1 >= nd) bsel = 1;
-            else { c += h1; bsel = 0; }
+            c += hv[2];
+            if (c + hv[1] >= nd) bsel = 1;
+            else { c += hv[1]; bsel = 0; }
         }
     }
     const uint64_t m = ballot(here);
     const int src = m ? __builtin_ctzll(m) : 0;
-    bin = __shfl(4 * lane + bsel, src, kWave);
-    above = __shfl(c, src, kWave);
+    bin = __builtin_amdgcn_readlane(b0 + bsel, src);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)c, src);
 }
 
-// In-place stable filter of buf[0..cnt): keeps keys > gt_than, plus the
-// first `eq_keep` keys equal to eq_key (eq_keep = 0 disables).  Returns the
-// new count; *kept_max = largest kept key.
-template <typename IdxT>
+// In-place stable filter of buf[0..cnt): keeps keys > gt_than, plus (TIES)
+// the first `eq_keep` keys equal to eq_key.  Returns the new count;
+// *kept_max = largest kept key.  The next step's entries are read before the
+// current step's kept entries are written: writes of a step land below
+// base + kStep, the next step reads from there upward, so they never overlap.
+template <bool TIES, typename IdxT>
 __device__ int filter4(uint32_t *bk, IdxT *bi, int cnt, uint32_t gt_than, uint32_t eq_key, int eq_keep, int lane,
                        uint32_t *kept_max) {
     int out = 0, eqseen = 0;
     uint32_t mx = 0;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t k[4];
+    IdxT ix[4];
+    if (cnt > 0) load4(bk, bi, 4 * lane, k, ix);
     for (int base = 0; base < cnt; base += kStep) {
         const int e0 = base + 4 * lane;
-        uint32_t k[4];
-        IdxT ix[4];
-        load4(bk, bi, e0, k, ix);
-        bool eq[4], keep[4];
-        int eqb = 0, keepb = 0;
-        uint64_t EM[4], KM[4];
+        uint32_t kn[4];
+        IdxT ixn[4];
+        if (base + kStep < cnt) load4(bk, bi, e0 + kStep, kn, ixn);
+        bool keep[4];
+        uint64_t KM[4];
+        int keepb = 0;
+        if constexpr (TIES) {
+            bool eq[4];
+            uint64_t EM[4];
+            int eqb = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool valid = e0 + j < cnt;
-            eq[j] = valid && eq_keep > 0 && k[j] == eq_key;
-            EM[j] = ballot(eq[j]);
+            for (int j = 0; j < 4; ++j) {
+                eq[j] = e0 + j < cnt && eq_keep > 0 && k[j] == eq_key;
+                EM[j] = ballot(eq[j]);
+                eqb += __popcll(EM[j] & lt);
+            }
+            int erank = eqseen + eqb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                keep[j] = e0 + j < cnt && (k[j] > gt_than || (eq[j] && erank < eq_keep));
+                erank += eq[j] ? 1 : 0;
+                eqseen += __popcll(EM[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) keep[j] = e0 + j < cnt && k[j] > gt_than;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) eqb += __popcll(EM[j] & lt);
-        int erank = eqseen + eqb;
-#pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bool valid = e0 + j < cnt;
-            keep[j] = valid && (k[j] > gt_than || (eq[j] && erank < eq_keep));
-            erank += eq[j] ? 1 : 0;
             KM[j] = ballot(keep[j]);
+            keepb += __popcll(KM[j] & lt);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) keepb += __popcll(KM[j] & lt);
         int pos = out + keepb;
-        // in-place: every write lands at or below an entry this step already read
         wave_lds_order();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -324,10 +347,55 @@ __device__ int filter4(uint32_t *bk, IdxT *bi, int cnt, uint32_t gt_than, uint32
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             out += __popcll(KM[j]);
-            eqseen += __popcll(EM[j]);
+            k[j] = kn[j];
+            ix[j] = ixn[j];
         }
     }
     if (kept_max) *kept_max = wave_max_u32(mx);
+    return out;
+}
+
+// In-place stable filter keeping keys > gt (no ties), for the binned
+// compaction.  Every lane writes all four of its entries each step: kept
+// ones to their compacted slot, dropped ones to its own slot in the padding
+// past the last row's buffer (pad_k / pad_i), so no write is predicated.
+// The next step's entries are read before this step's writes (those land
+// below base + kStep).  Returns the new count.
+template <typename IdxT>
+__device__ int filter_gt(uint32_t *bk, IdxT *bi, int cnt, uint32_t gt, uint32_t *pad_k, IdxT *pad_i, int lane) {
+    int out = 0;
+    uint32_t k[4];
+    IdxT ix[4];
+    if (cnt > 0) load4(bk, bi, 4 * lane, k, ix);
+    for (int base = 0; base < cnt; base += kStep) {
+        const int e0 = base + 4 * lane;
+        uint32_t kn[4];
+        IdxT ixn[4];
+        if (base + kStep < cnt) load4(bk, bi, e0 + kStep, kn, ixn);
+        const uint64_t K0 = ballot(e0 < cnt && k[0] > gt);
+        const uint64_t K1 = ballot(e0 + 1 < cnt && k[1] > gt);
+        const uint64_t K2 = ballot(e0 + 2 < cnt && k[2] > gt);
+        const uint64_t K3 = ballot(e0 + 3 < cnt && k[3] > gt);
+        const int kp0 = (int)((K0 >> lane) & 1u), kp1 = (int)((K1 >> lane) & 1u);
+        const int kp2 = (int)((K2 >> lane) & 1u), kp3 = (int)((K3 >> lane) & 1u);
+        const int p0 = out + lanes_below(K0) + lanes_below(K1) + lanes_below(K2) + lanes_below(K3);
+        const int p1 = p0 + kp0, p2 = p1 + kp1, p3 = p2 + kp2;
+        uint32_t *a0 = kp0 ? bk + p0 : pad_k + lane;
+        uint32_t *a1 = kp1 ? bk + p1 : pad_k + lane;
+        uint32_t *a2 = kp2 ? bk + p2 : pad_k + lane;
+        uint32_t *a3 = kp3 ? bk + p3 : pad_k + lane;
+        IdxT *c0 = kp0 ? bi + p0 : pad_i + lane;
+        IdxT *c1 = kp1 ? bi + p1 : pad_i + lane;
+        IdxT *c2 = kp2 ? bi + p2 : pad_i + lane;
+        IdxT *c3 = kp3 ? bi + p3 : pad_i + lane;
+        wave_lds_order();
+        *a0 = k[0]; *a1 = k[1]; *a2 = k[2]; *a3 = k[3];
+        *c0 = ix[0]; *c1 = ix[1]; *c2 = ix[2]; *c3 = ix[3];
+        wave_lds_order();
+        out += __popcll(K0) + __popcll(K1) + __popcll(K2) + __popcll(K3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { k[j] = kn[j]; ix[j] = ixn[j]; }
+    }
     return out;
 }
 
@@ -378,18 +446,20 @@ __device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, 
         top = shift;
         wave_lds_order();
     }
-    cnt = filter4<IdxT>(bkey, bidx, cnt, prefix, prefix, need, lane, kept_max);
+    cnt = filter4<true, IdxT>(bkey, bidx, cnt, prefix, prefix, need, lane, kept_max);
     return prefix;
 }
 
 // Binned-selection state of one row (wave-uniform, one row per wavefront).
+// Once `binned`, the wave's 256-bin histogram counts every buffered key by
+// its bin above the window base `lo` (log-spaced bins, see bin_of); appends
+// keep it current, so a compaction reads the cut off it directly.
 struct BinState {
     int cnt;          // entries in the buffer
     uint32_t thr;     // append filter: key > thr
     float thr_f;      // the same filter on scores: score > thr_f
-    uint32_t maxkey;  // largest key kept by the last compaction
-    int shift;        // histogram bin width 2^shift (set from maxkey and thr)
-    bool binned;      // an exact selection has run (thr is a real threshold)
+    uint32_t lo;      // histogram base (<= every buffered key)
+    bool binned;      // the histogram is live
 };
 
 // Largest float whose order-preserving key is <= thr: for every finite f,
@@ -401,59 +471,97 @@ __device__ __forceinline__ float key_floor_float(uint32_t thr) {
     return __uint_as_float(~thr);
 }
 
-__device__ __forceinline__ int window_shift(uint32_t maxkey, uint32_t lo) {
-    const uint32_t span = maxkey > lo ? maxkey - lo : 0u;
-    const int bits = span ? 32 - __builtin_clz(span) : 0;
-    return bits > 8 ? bits - 8 : 0;
+// Log-spaced bins of d = key - lo: d < 8 has its own bin; above that, eight
+// bins per power of two (d's leading bit plus the next three bits), so the
+// bins are finest just above the base, where the cut falls.  Bin order is
+// key order; 8 + 8 * 29 bins cover every 32-bit d.
+__device__ __forceinline__ uint32_t bin_of(uint32_t key, uint32_t lo) {
+    const uint32_t d = key - lo;
+    if (d < 8u) return d;
+    const int e = 31 - __builtin_clz(d);
+    return 8u * (uint32_t)(e - 2) + ((d >> (e - 3)) & 7u);
 }
 
-template <typename IdxT>
-__device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, uint32_t *hist, int lane) {
-    const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane, &st.maxkey);
-    st.thr = theta;
-    st.thr_f = key_floor_float(theta);
-    st.binned = true;
+// smallest d of bin b
+__device__ __forceinline__ uint32_t bin_floor(int b) {
+    if (b < 8) return (uint32_t)b;
+    const int e = b / 8 + 2;
+    return (uint32_t)(8 + (b & 7)) << (e - 3);
 }
 
-// Shrink the buffer by binning: every buffered key is >= thr (keys equal to
-// it are ties kept by an exact selection), so bin keys over the window
-// [thr, thr + 256 << shift) (shift from the last kept maximum; larger keys
-// share the top bin), find the bin holding the k-th largest key and keep
-// every entry at or above that bin's lower edge: at least k entries, all
-// better than anything dropped.  Exact selection when this frees too little
-// room.  Precondition: st.cnt >= k.
+// Histogram of the buffer above base lo.
 template <typename IdxT>
-__device__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
-                               int lane) {
-    if (!st.binned) {
-        compact_exact<IdxT>(bkey, bidx, st, k, hist, lane);
-        return;
-    }
-    const uint32_t lo = st.thr;
-    const int shift = window_shift(st.maxkey, lo);
+__device__ void rebuild_hist(const uint32_t *bkey, BinState &st, uint32_t lo, uint32_t *hist, int lane) {
+    st.lo = lo;
     for (int j = lane; j < kHistWords; j += kWave) hist[j] = 0;
     wave_lds_order();
     for (int base = 0; base < st.cnt; base += kStep) {
         const int e0 = base + 4 * lane;
         const v4u kk = *reinterpret_cast<const v4u *>(bkey + e0);
 #pragma unroll
+        for (int j = 0; j < 4; ++j) atomicAdd(&hist[e0 + j < st.cnt ? bin_of(kk[j], lo) : 256u + lane], 1u);
+    }
+    wave_lds_order();
+    st.binned = true;
+}
+
+template <typename IdxT>
+__device__ uint32_t buffer_min(const uint32_t *bkey, int cnt, int lane) {
+    uint32_t mn = 0xFFFFFFFFu;
+    for (int base = 0; base < cnt; base += kStep) {
+        const int e0 = base + 4 * lane;
+        const v4u kk = *reinterpret_cast<const v4u *>(bkey + e0);
+#pragma unroll
         for (int j = 0; j < 4; ++j)
-            atomicAdd(&hist[e0 + j < st.cnt ? min((kk[j] - lo) >> shift, 255u) : 256u + lane], 1u);
+            if (e0 + j < cnt) mn = min(mn, kk[j]);
     }
-    wave_lds_order();
-    int bstar;
-    uint32_t above;
-    hist_find(hist, k, lane, bstar, above);
-    const uint32_t nkeep = above + hist[bstar];
-    wave_lds_order();
-    if (bstar == 0 || bstar == 255 || (int)nkeep > cap - 2 * KB) {
-        compact_exact<IdxT>(bkey, bidx, st, k, hist, lane);
-        return;
+    return ~wave_max_u32(~mn);
+}
+
+template <typename IdxT>
+__device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, uint32_t *hist, int lane) {
+    const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane);
+    st.thr = theta;
+    st.thr_f = key_floor_float(theta);
+    rebuild_hist<IdxT>(bkey, st, theta, hist, lane);
+}
+
+// Shrink the buffer off the live histogram: the bin holding the k-th largest
+// key is read off it, every entry at or above that bin's lower edge is kept
+// (at least k entries, all better than anything dropped), the emptied bins
+// are cleared, and the edge bounds the threshold.  Bins are log-spaced above
+// the base; once the cut has climbed into the coarser bins the histogram is
+// rebuilt from the new threshold, and when the cut's bin holds too many
+// entries (too little room freed) it is rebuilt from the current threshold
+// and read again; exact selection is the last resort.
+// Precondition: st.cnt >= k.
+template <typename IdxT>
+__device__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
+                               uint32_t *pad_k, IdxT *pad_i, int lane) {
+    if (!st.binned) rebuild_hist<IdxT>(bkey, st, buffer_min<IdxT>(bkey, st.cnt, lane), hist, lane);
+    for (int attempt = 0;; ++attempt) {
+        int bstar;
+        uint32_t above;
+        hist_find(hist, k, lane, bstar, above);
+        const uint32_t nkeep = above + hist[bstar];
+        wave_lds_order();
+        if (bstar > 0 && (int)nkeep <= cap - 2 * KB) {
+            const uint32_t edge = st.lo + bin_floor(bstar);   // keep keys >= edge
+            st.cnt = filter_gt<IdxT>(bkey, bidx, st.cnt, edge - 1u, pad_k, pad_i, lane);
+            st.thr = edge - 1u;
+            st.thr_f = key_floor_float(st.thr);
+            if (bstar >= 96) {
+                rebuild_hist<IdxT>(bkey, st, st.thr, hist, lane);   // re-centre: finest bins at the cut
+            } else {
+                for (int j = lane; j < bstar; j += kWave) hist[j] = 0;
+                wave_lds_order();
+            }
+            return;
+        }
+        if (attempt > 0 || st.thr <= st.lo) break;
+        rebuild_hist<IdxT>(bkey, st, st.thr, hist, lane);   // finer bins just above the threshold
     }
-    const uint32_t edge = lo + ((uint32_t)bstar << shift);   // keep keys >= edge
-    st.cnt = filter4<IdxT>(bkey, bidx, st.cnt, edge - 1u, 0u, 0, lane, &st.maxkey);
-    st.thr = edge - 1u;
-    st.thr_f = key_floor_float(st.thr);
+    compact_exact<IdxT>(bkey, bidx, st, k, hist, lane);
 }
 
 struct PrefillParams {
@@ -560,7 +668,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     if (tid < 3) flags[tid] = 0;
     BinState st;
-    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.maxkey = 0u; st.shift = 0; st.binned = false;
+    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u; st.binned = false;
     const int want_level = p.topk + (p.cap - p.topk) / 2;
 
     // stage key block 0.  Thread tid stages 16-byte chunks tid + c*blockDim
@@ -701,11 +809,12 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                         uint32_t *bk = bkey_all + (size_t)wave * p.cap;
                         IdxT *bi = bidx_all + (size_t)wave * p.cap;
                         const int at = st.cnt + lanes_below(m);
+                        const uint32_t key = score_key(sc[0]);
                         if (cand) {
-                            const uint32_t key = score_key(sc[0]);
                             bk[at] = key;
                             bi[at] = (IdxT)s;
                         }
+                        if (st.binned) atomicAdd(&hist[cand ? bin_of(key, st.lo) : 256u + lane], 1u);
                         st.cnt += __popcll(m);
                     }
                     need = st.cnt > p.cap - KB;
@@ -753,7 +862,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         if constexpr (kBinned) {
             if (flags[blk % 3] && st.cnt > want_level) {
                 compact_binned<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, st, p.topk,
-                                     p.cap, hist, lane);
+                                     p.cap, hist, bkey_all + (size_t)R * p.cap, bidx_all + (size_t)R * p.cap, lane);
             }
         }
     }
@@ -763,9 +872,9 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         const int i = i0 + wave * TW + t;
         if (i >= p.Lq) break;
         const int row = wave * TW + t;
-        int cnt = kBinned ? st.cnt : rcnt[row];
         uint32_t *bk = bkey_all + (size_t)row * p.cap;
         IdxT *bi = bidx_all + (size_t)row * p.cap;
+        int cnt = kBinned ? st.cnt : rcnt[row];
         if (cnt > p.topk) (void)select_compact<IdxT>(bk, bi, cnt, p.topk, hist, lane);
         int32_t *o = p.t_out + ((size_t)b * p.Lq + i) * p.topk;
         for (int j = lane; j < p.topk; j += kWave) o[j] = j < cnt ? (int32_t)bi[j] : -1;
