@@ -45,6 +45,11 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     ap.add_argument("--profile-only", action="store_true", help="run warmup+steps of the headline only")
+    ap.add_argument("--profile", choices=["prefill", "decode", "copy"],
+                    help="run warmup+steps of one workload (for profiler runs) and exit")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="write the headline kernel's HBM traffic from rocprofv3 counter runs in DIR "
+                         "(subdirectories fetch/, write/, copy_fetch/, copy_write/) and exit")
     return ap.parse_args()
 
 
@@ -131,6 +136,75 @@ def decode(args, torch, sa, inputs):
     }
 
 
+COPY_BYTES = 1 << 30   # the calibration copy moves this many bytes each way
+
+
+def profile_run(args, torch, sa, inputs):
+    """Runs one workload a few times with no timing, for rocprofv3."""
+    dev = torch.device("cuda:0")
+    if args.profile == "prefill":
+        headline(args, torch, sa, inputs)
+    elif args.profile == "decode":
+        wl = inputs.WORKLOADS["decode_200k"]
+        q, k, w = inputs.indexer_inputs(wl, 0, dev)
+        qa, kv = inputs.attention_inputs(wl, 0, dev)
+        t = torch.empty(wl.B, wl.Lq, wl.topk, dtype=torch.int32, device=dev)
+        out = torch.empty(wl.B, wl.Lq, wl.Hq, wl.Dv, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(sa.idx_score_topk_workspace(q, k, w, wl.topk), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup + args.steps):
+            sa.idx_cache_route("F", 0, q, k, w, t, ws=ws)
+            sa.sparse_mla_attn(qa, kv, t, 1.0 / math.sqrt(wl.Dqk), wl.Dv, out=out)
+    else:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profiled": args.profile, "runs": args.warmup + args.steps}))
+
+
+def _counter_kb(run_dir, counter, name_part):
+    """Mean per-dispatch value of `counter` over dispatches whose kernel name contains name_part
+    (counter values of one dispatch summed over the rows rocprofv3 writes for it)."""
+    import csv
+    import glob
+    per_dispatch = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter and name_part in r.get("Kernel_Name", ""):
+                    key = (path, r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+                    per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    if not per_dispatch:
+        raise SystemExit(f"no {counter} rows for '{name_part}' under {run_dir}")
+    return sum(per_dispatch.values()) / len(per_dispatch)
+
+
+def traffic_from(args):
+    """Scales the headline kernel's FETCH_SIZE / WRITE_SIZE by what the same
+    counters read for a copy of COPY_BYTES, and records the result."""
+    d = args.traffic_from
+    kname = "prefill_kernel"
+    copy_name = "copyBuffer"   # the device-to-device copy torch issues for dst.copy_(src)
+    fetch_kb = _counter_kb(os.path.join(d, "fetch"), "FETCH_SIZE", kname)
+    write_kb = _counter_kb(os.path.join(d, "write"), "WRITE_SIZE", kname)
+    cf_kb = _counter_kb(os.path.join(d, "copy_fetch"), "FETCH_SIZE", copy_name)
+    cw_kb = _counter_kb(os.path.join(d, "copy_write"), "WRITE_SIZE", copy_name)
+    f_fetch = cf_kb * 1024.0 / COPY_BYTES
+    f_write = cw_kb * 1024.0 / COPY_BYTES
+    read_b = fetch_kb * 1024.0 / f_fetch
+    write_b = write_kb * 1024.0 / f_write
+    rec = {"kernel": kname, "workload": "prefill_64k", "kernel_source_sha": _kernel_sha(),
+           "fetch_size_kb": fetch_kb, "write_size_kb": write_kb,
+           "copy_bytes_each_way": COPY_BYTES, "copy_fetch_kb": cf_kb, "copy_write_kb": cw_kb,
+           "scale_fetch": f_fetch, "scale_write": f_write,
+           "read_bytes_per_launch": read_b, "write_bytes_per_launch": write_b,
+           "bytes_per_launch": read_b + write_b}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(args, inputs, torch):
     """Oracle rows/s on the host, scaled to pairs/s (bounded seeded row sample)."""
     import numpy as np
@@ -161,6 +235,9 @@ def cpu_baseline(args, inputs, torch):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
@@ -170,6 +247,9 @@ def main():
     from sparse_attention_indexer_lightning_amd import inputs
 
     sa.lib()
+    if args.profile:
+        profile_run(args, torch, sa, inputs)
+        return
     wl, ms, pairs, flops = headline(args, torch, sa, inputs)
     if args.profile_only:
         print(json.dumps({"ms_per_step": ms}))
