@@ -98,7 +98,8 @@ idxc_status idx_score_topk(const idxc_indexer_desc *desc, const void *q, const v
                            const void *w, int32_t *t_out, float *scores_dbg, void *ws,
                            size_t ws_bytes, void *stream);
 
-/* Workspace bytes for idx_topk (may be 0). */
+/* Workspace bytes for idx_topk (may be 0: it is nonzero when few long rows
+ * are each split over several workgroups). */
 idxc_status idx_topk_workspace(int R, int Lk, int topk, size_t *bytes);
 
 /*
@@ -109,6 +110,9 @@ idxc_status idx_topk_workspace(int R, int Lk, int topk, size_t *bytes);
  *           means Lk - 1 for every row.  Values must lie in [-1, Lk - 1].
  *   t_out   int32 [R, topk]: if row_pos + 1 <= topk: 0..row_pos then -1;
  *           otherwise the topk keys by (score desc, index asc), ascending.
+ *   ws      device scratch of ws_bytes >= idx_topk_workspace(R, Lk, topk)
+ *           bytes, 16-byte aligned; may be NULL when that size is 0.  Its
+ *           contents are overwritten; IDXC_ERR_WORKSPACE when too small.
  * -0 and +0 compare equal.  NaN scores are outside the contract.
  */
 idxc_status idx_topk(const float *scores, const int32_t *row_pos, int R, int Lk, int topk,

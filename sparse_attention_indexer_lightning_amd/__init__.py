@@ -152,13 +152,15 @@ def idx_topk_workspace(R: int, Lk: int, topk: int) -> int:
     return n.value
 
 
-def idx_topk(scores, topk: int, row_pos=None, t_out=None, stream=None):
+def idx_topk(scores, topk: int, row_pos=None, t_out=None, ws=None, stream=None):
     """Row top-k of fp32 scores [R, Lk] (ties to the lower index, ascending, -1 padded)."""
     _cuda_tensor(scores, "scores")
     R, Lk = scores.shape
     if t_out is None:
         t_out = torch.empty(R, topk, dtype=torch.int32, device=scores.device)
-    _check(lib().idx_topk(_p(scores), _p(row_pos), R, Lk, topk, _p(t_out), None, 0,
+    ws = _workspace(idx_topk_workspace(R, Lk, topk), scores.device, ws)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().idx_topk(_p(scores), _p(row_pos), R, Lk, topk, _p(t_out), _p(ws), wsb,
                           _stream(stream, scores.device)), "idx_topk")
     return t_out
 

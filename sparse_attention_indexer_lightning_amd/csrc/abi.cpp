@@ -68,8 +68,13 @@ Path choose_path(const idxc::IndexerArgs &a) {
     return Path::None;
 }
 
+// Decode workspace: the score rows, then the row top-k's own workspace.
+size_t decode_scores_bytes(const idxc_indexer_desc *d) {
+    return ((size_t)d->B * d->Lq * d->Lk * sizeof(float) + 255) & ~(size_t)255;
+}
+
 size_t decode_ws_bytes(const idxc_indexer_desc *d) {
-    return (size_t)d->B * d->Lq * d->Lk * sizeof(float);
+    return decode_scores_bytes(d) + idxc::row_topk_ws_bytes(d->B * d->Lq, d->Lk);
 }
 
 idxc_status from_hip(hipError_t e) { return e == hipSuccess ? IDXC_OK : IDXC_ERR_HIP; }
@@ -111,10 +116,13 @@ idxc_status run_indexer(const idxc_indexer_desc *d, const void *q, const void *k
     ta.topk = d->topk;
     ta.pos_Lq = d->Lq;
     ta.t_out = t;
+    ta.ws = static_cast<unsigned char *>(ws) + decode_scores_bytes(d);
+    ta.ws_bytes = idxc::row_topk_ws_bytes(ta.R, ta.Lk);
     e = idxc::launch_row_topk(ta, stream);
     if (e != hipSuccess) return IDXC_ERR_HIP;
     if (scores_dbg)
-        e = hipMemcpyAsync(scores_dbg, scores, decode_ws_bytes(d), hipMemcpyDeviceToDevice, stream);
+        e = hipMemcpyAsync(scores_dbg, scores, (size_t)d->B * d->Lq * d->Lk * sizeof(float), hipMemcpyDeviceToDevice,
+                           stream);
     return from_hip(e);
 }
 
@@ -162,19 +170,22 @@ idxc_status idx_topk_workspace(int R, int Lk, int topk, size_t *bytes) {
     if (!bytes) return IDXC_ERR_NULL;
     if (R < 0 || Lk < 1 || topk < 1 || Lk > kMaxLen) return IDXC_ERR_SHAPE;
     if (topk > kMaxTopk) return IDXC_ERR_UNSUPPORTED;
-    *bytes = 0;
+    *bytes = idxc::row_topk_ws_bytes(R, Lk);
     return IDXC_OK;
 }
 
 idxc_status idx_topk(const float *scores, const int32_t *row_pos, int R, int Lk, int topk, int32_t *t_out,
                      void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (R < 0 || Lk < 1 || topk < 1 || Lk > kMaxLen) return IDXC_ERR_SHAPE;
     if (topk > kMaxTopk) return IDXC_ERR_UNSUPPORTED;
     if (R == 0) return IDXC_OK;
     if (!scores || !t_out) return IDXC_ERR_NULL;
     if (!aligned(scores, 4) || !aligned(t_out, 4) || (row_pos && !aligned(row_pos, 4))) return IDXC_ERR_ALIGN;
+    const size_t need = idxc::row_topk_ws_bytes(R, Lk);
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return IDXC_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return IDXC_ERR_ALIGN;
+    }
     idxc::TopkArgs a;
     a.scores = scores;
     a.row_pos = row_pos;
@@ -183,6 +194,8 @@ idxc_status idx_topk(const float *scores, const int32_t *row_pos, int R, int Lk,
     a.topk = topk;
     a.pos_Lq = 0;
     a.t_out = t_out;
+    a.ws = ws;
+    a.ws_bytes = ws_bytes;
     return from_hip(idxc::launch_row_topk(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -30,13 +30,18 @@ hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t s);
 // Exact per-row top-k of fp32 scores [R, Lk] (ties to the lower index,
 // ascending output, -1 padding).  row_pos may be NULL (all Lk keys valid).
 // pos_from_query != 0 derives the position of row r as (Lk - Lq + r % Lq).
+// Long rows that are few in number are split over several workgroups; that
+// needs row_topk_ws_bytes(R, Lk) bytes of workspace (0 when not split).
 struct TopkArgs {
     const float *scores;
     const int32_t *row_pos;
     int R, Lk, topk;
     int pos_Lq;       // > 0: row position = Lk - pos_Lq + r % pos_Lq (row_pos unused)
     int32_t *t_out;
+    void *ws;         // device workspace of ws_bytes bytes (16-byte aligned), may be NULL if not needed
+    size_t ws_bytes;
 };
+size_t row_topk_ws_bytes(int R, int Lk);
 hipError_t launch_row_topk(const TopkArgs &a, hipStream_t s);
 
 struct MlaArgs {

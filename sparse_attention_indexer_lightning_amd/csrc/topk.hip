@@ -5,7 +5,20 @@
 // "Einfache Implementierung, enorme Effizienzgewinne": T = top-k(I), with ties
 // going to the lower key index and T written in ascending index order.
 //
-// One workgroup (16 wavefronts) per row, on order-preserving 32-bit keys:
+// Everything runs on order-preserving 32-bit keys of the scores.
+//
+// Few long rows (decode: 32 rows of 200K scores) are split over S workgroups
+// each, in three launches:
+//  1. bound: split s of a row computes a lower bound b_s on its own m-th
+//     largest key, m = ceil(k / S) (the m-th largest of the union of
+//     per-thread top-4 lists, a subset of the split).  At least m keys of the
+//     split are >= b_s, so at least S*m >= k keys of the row are >= min_s b_s:
+//     theta = min_s b_s never exceeds the row's k-th largest key;
+//  2. collect: every split writes its keys >= theta, in index order, to its
+//     own region of the workspace;
+//  3. select: one workgroup per row loads the candidates of all splits (in
+//     split order, so in index order) into LDS and runs the exact selection.
+// Otherwise one workgroup (16 wavefronts) handles a whole row:
 //  1. bound: every thread keeps the 4 largest keys of its strided share of
 //     the row; the k-th largest of these 4096 keys is <= the row's k-th
 //     largest key (they are a subset of the row), so every member of the
@@ -47,15 +60,26 @@ __device__ __forceinline__ uint32_t wave_max32(uint32_t v) {
     return v;
 }
 
+// Insert u into a descending list of the 4 largest keys seen.
+__device__ __forceinline__ void keep_top4(uint32_t (&top)[kLocal], uint32_t u) {
+    if (u > top[3]) {
+        top[3] = u;
+        if (top[3] > top[2]) { const uint32_t x = top[2]; top[2] = top[3]; top[3] = x; }
+        if (top[2] > top[1]) { const uint32_t x = top[1]; top[1] = top[2]; top[2] = x; }
+        if (top[1] > top[0]) { const uint32_t x = top[0]; top[0] = top[1]; top[1] = x; }
+    }
+}
+
 // The need-th largest key among `n` keys produced by get(i) (block-wide),
 // returning the key and, through *above, how many keys are strictly larger.
 // MSB-first radix select with 11-bit digits, starting below the bits that the
 // smallest and largest key share (so the first digit already spreads keys).
-template <typename Get>
-__device__ uint32_t block_select(TopkShared &sh, int n, int need, Get get, uint32_t *above_out) {
+template <int NT = kThreads, typename Sh, typename Get>
+__device__ uint32_t block_select(Sh &sh, int n, int need, Get get, uint32_t *above_out) {
+    constexpr int NW = NT / kWave;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int i = tid; i < n; i += kThreads) {
+    for (int i = tid; i < n; i += NT) {
         const uint32_t u = get(i);
         mn = min(mn, u);
         mx = max(mx, u);
@@ -65,7 +89,7 @@ __device__ uint32_t block_select(TopkShared &sh, int n, int need, Get get, uint3
     if (lane == 0) { sh.wtot[0][wave] = mn; sh.wtot[1][wave] = mx; }
     __syncthreads();
     mn = 0xFFFFFFFFu; mx = 0u;
-    for (int w = 0; w < kWaves; ++w) { mn = min(mn, sh.wtot[0][w]); mx = max(mx, sh.wtot[1][w]); }
+    for (int w = 0; w < NW; ++w) { mn = min(mn, sh.wtot[0][w]); mx = max(mx, sh.wtot[1][w]); }
     int top = (mn == mx) ? 0 : 32 - __builtin_clz(mn ^ mx);
     uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
     uint32_t prefix = mn & pmask;
@@ -74,9 +98,9 @@ __device__ uint32_t block_select(TopkShared &sh, int n, int need, Get get, uint3
         const int width = top < kDigit ? top : kDigit;
         const int shift = top - width;
         const uint32_t dmask = (1u << width) - 1u;
-        for (int j = tid; j < kBins; j += kThreads) sh.hist[j] = 0;
+        for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kThreads) {
+        for (int i = tid; i < n; i += NT) {
             const uint32_t u = get(i);
             if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & dmask], 1u);
         }
@@ -174,14 +198,7 @@ __global__ __launch_bounds__(kThreads) void row_topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) u[e] = j0 + e < n ? score_key(s[j0 + e]) : 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (u[e] > top[3]) {
-                top[3] = u[e];
-                if (top[3] > top[2]) { const uint32_t x = top[2]; top[2] = top[3]; top[3] = x; }
-                if (top[2] > top[1]) { const uint32_t x = top[1]; top[1] = top[2]; top[2] = x; }
-                if (top[1] > top[0]) { const uint32_t x = top[0]; top[0] = top[1]; top[1] = x; }
-            }
-        }
+        for (int e = 0; e < 4; ++e) keep_top4(top, u[e]);
     }
 #pragma unroll
     for (int i = 0; i < kLocal; ++i) sh.ukey[tid * kLocal + i] = top[i];
@@ -246,11 +263,227 @@ __global__ __launch_bounds__(kThreads) void row_topk_kernel(TopkArgs a) {
                    [&](int i) { return i; }, out);
 }
 
+// ------------------------------------------------------------ split rows
+
+constexpr int kSplitThreads = 256;
+constexpr int kSplitWaves = kSplitThreads / kWave;
+constexpr int kMinSplit = 4096;        // keys per split at least
+constexpr int kSplitTarget = 512;      // aim for about this many workgroups in total
+constexpr int kSplitVec = 16;          // keys per thread per step (loads in flight)
+
+struct SplitShared {
+    uint32_t ukey[kSplitThreads * kLocal];
+    uint32_t hist[kBins];
+    uint32_t wtot[2][kSplitWaves];
+    int sh_bin;
+    uint32_t sh_above;
+};
+
+struct SplitPlan {
+    int S;          // splits per row (1: whole-row kernel)
+    int N;          // keys per split
+};
+
+__host__ inline SplitPlan split_plan(int R, int Lk) {
+    SplitPlan pl{1, Lk};
+    if (R <= 0 || R >= kSplitTarget / 2 || Lk < 4 * kMinSplit) return pl;
+    int S = (kSplitTarget + R - 1) / R;
+    if (S > Lk / kMinSplit) S = Lk / kMinSplit;
+    if (S < 2) return pl;
+    pl.S = S;
+    pl.N = (Lk + S - 1) / S;
+    return pl;
+}
+
+struct SplitWs {
+    uint32_t *bound;     // [R][S]
+    int *count;          // [R][S]
+    uint2 *cand;         // [R][S][N]: (key, index)
+    size_t bytes;
+};
+
+__host__ __device__ inline SplitWs split_ws(void *base, int R, const SplitPlan &pl) {
+    SplitWs w;
+    unsigned char *p = static_cast<unsigned char *>(base);
+    const size_t rs = (size_t)R * pl.S;
+    size_t off = 0;
+    w.bound = reinterpret_cast<uint32_t *>(p + off);
+    off += (rs * 4 + 255) & ~(size_t)255;
+    w.count = reinterpret_cast<int *>(p + off);
+    off += (rs * 4 + 255) & ~(size_t)255;
+    w.cand = reinterpret_cast<uint2 *>(p + off);
+    off += rs * pl.N * 8;
+    w.bytes = off;
+    return w;
+}
+
+__device__ __forceinline__ int row_valid(const TopkArgs &a, int r) {
+    int pos;
+    if (a.pos_Lq > 0) pos = a.Lk - a.pos_Lq + r % a.pos_Lq;
+    else pos = a.row_pos ? a.row_pos[r] : a.Lk - 1;
+    pos = min(pos, a.Lk - 1);
+    return pos + 1 > 0 ? pos + 1 : 0;
+}
+
+// 1. per split: a lower bound on its m-th largest key.  Only the F = n / N
+// completely filled splits of a row vouch for keys, m = ceil(k / F) each;
+// the others report the neutral maximum.  With F = 0, or m beyond the
+// per-thread lists, the bound is 0 (no pruning for the row).
+__global__ __launch_bounds__(kSplitThreads) void topk_split_bound(TopkArgs a, SplitPlan pl, SplitWs ws) {
+    __shared__ SplitShared sh;
+    const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const int n = row_valid(a, r);
+    const int full = n / pl.N;
+    uint32_t *dst = ws.bound + (size_t)r * pl.S + s;
+    if (full == 0 || s >= full) {
+        if (tid == 0) *dst = (full == 0 && s == 0) ? 0u : 0xFFFFFFFFu;
+        return;
+    }
+    const int m = (a.topk + full - 1) / full;
+    if (m > kSplitThreads * kLocal) {
+        if (tid == 0) *dst = 0u;
+        return;
+    }
+    const int j0 = s * pl.N, j1 = j0 + pl.N;
+    const float *row = a.scores + (size_t)r * a.Lk;
+    uint32_t top[kLocal] = {0u, 0u, 0u, 0u};
+    for (int c0 = j0; c0 < j1; c0 += kSplitVec * kSplitThreads) {
+        float v[kSplitVec];
+#pragma unroll
+        for (int e = 0; e < kSplitVec; ++e) {
+            const int j = c0 + e * kSplitThreads + tid;
+            v[e] = j < j1 ? row[j] : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < kSplitVec; ++e) keep_top4(top, score_key(v[e]));
+    }
+#pragma unroll
+    for (int i = 0; i < kLocal; ++i) sh.ukey[tid * kLocal + i] = top[i];
+    __syncthreads();
+    uint32_t dummy;
+    const uint32_t b = block_select<kSplitThreads>(sh, kSplitThreads * kLocal, m, [&](int i) { return sh.ukey[i]; },
+                                                   &dummy);
+    if (tid == 0) *dst = b;
+}
+
+// 2. per split: keys >= theta = min over the row's bounds, in index order.
+// Each step thread t looks at keys c0 + e * 256 + t (e < kSplitVec), so the
+// order is e-major; a per-(e, wave) count table gives every key its slot.
+__global__ __launch_bounds__(kSplitThreads) void topk_split_collect(TopkArgs a, SplitPlan pl, SplitWs ws) {
+    __shared__ uint32_t wcnt[2][kSplitVec][kSplitWaves];
+    const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int n = row_valid(a, r);
+    const int j0 = s * pl.N, j1 = min(j0 + pl.N, n);
+    uint32_t theta = 0xFFFFFFFFu;
+    for (int i = 0; i < pl.S; ++i) theta = min(theta, ws.bound[(size_t)r * pl.S + i]);
+    const float *row = a.scores + (size_t)r * a.Lk;
+    uint2 *out = ws.cand + ((size_t)r * pl.S + s) * pl.N;
+    uint32_t base = 0;
+    int par = 0;
+    for (int c0 = j0; c0 < j1; c0 += kSplitVec * kSplitThreads, par ^= 1) {
+        float v[kSplitVec];
+#pragma unroll
+        for (int e = 0; e < kSplitVec; ++e) {
+            const int j = c0 + e * kSplitThreads + tid;
+            v[e] = j < j1 ? row[j] : -INFINITY;
+        }
+        uint32_t u[kSplitVec];
+        uint64_t B[kSplitVec];
+#pragma unroll
+        for (int e = 0; e < kSplitVec; ++e) {
+            const int j = c0 + e * kSplitThreads + tid;
+            u[e] = score_key(v[e]);
+            B[e] = ballot(j < j1 && u[e] >= theta);
+            if (lane == 0) wcnt[par][e][wave] = (uint32_t)__popcll(B[e]);
+        }
+        __syncthreads();
+        uint32_t before = base;   // keys kept ahead of (e, wave) in this step
+#pragma unroll
+        for (int e = 0; e < kSplitVec; ++e) {
+            uint32_t tot = 0, wb = 0;
+#pragma unroll
+            for (int w = 0; w < kSplitWaves; ++w) {
+                const uint32_t c = wcnt[par][e][w];
+                if (w < wave) wb += c;
+                tot += c;
+            }
+            if ((B[e] >> lane) & 1u) {
+                const int j = c0 + e * kSplitThreads + tid;
+                out[before + wb + (uint32_t)lanes_below(B[e])] = make_uint2(u[e], (uint32_t)j);
+            }
+            before += tot;
+        }
+        base = before;
+    }
+    if (tid == 0) ws.count[(size_t)r * pl.S + s] = (int)base;
+}
+
+// 3. per row: exact selection over all splits' candidates.
+__global__ __launch_bounds__(kThreads) void topk_split_select(TopkArgs a, SplitPlan pl, SplitWs ws) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    TopkShared &sh = *reinterpret_cast<TopkShared *>(smem_raw);
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int n = row_valid(a, r);
+    const int k = a.topk;
+    int32_t *out = a.t_out + (size_t)r * k;
+    if (n <= k) {
+        for (int j = tid; j < k; j += kThreads) out[j] = j < n ? j : -1;
+        return;
+    }
+    int total = 0;
+    for (int i = 0; i < pl.S; ++i) total += ws.count[(size_t)r * pl.S + i];
+    if (total <= kCandCap) {
+        // gather the candidates of every split, in split order
+        int off = 0;
+        for (int i = 0; i < pl.S; ++i) {
+            const int c = ws.count[(size_t)r * pl.S + i];
+            const uint2 *src = ws.cand + ((size_t)r * pl.S + i) * pl.N;
+            for (int j = tid; j < c; j += kThreads) {
+                const uint2 v = src[j];
+                sh.ckey[off + j] = v.x;
+                sh.cidx[off + j] = (int32_t)v.y;
+            }
+            off += c;
+        }
+        __syncthreads();
+        uint32_t above;
+        const uint32_t theta = block_select(sh, total, k, [&](int i) { return sh.ckey[i]; }, &above);
+        ordered_output(sh, total, theta, k - (int)above, k, [&](int i) { return sh.ckey[i]; },
+                       [&](int i) { return sh.cidx[i]; }, out);
+        return;
+    }
+    // too many candidates for LDS: radix selection over the row in HBM
+    const float *srow = a.scores + (size_t)r * a.Lk;
+    uint32_t above;
+    const uint32_t theta = block_select(sh, n, k, [&](int i) { return score_key(srow[i]); }, &above);
+    ordered_output(sh, n, theta, k - (int)above, k, [&](int i) { return score_key(srow[i]); },
+                   [&](int i) { return i; }, out);
+}
+
 }  // namespace
+
+size_t row_topk_ws_bytes(int R, int Lk) {
+    const SplitPlan pl = split_plan(R, Lk);
+    if (pl.S == 1) return 0;
+    return split_ws(nullptr, R, pl).bytes;
+}
 
 hipError_t launch_row_topk(const TopkArgs &a, hipStream_t st) {
     if (a.R <= 0) return hipSuccess;
     const size_t lds = sizeof(TopkShared);
+    const SplitPlan pl = split_plan(a.R, a.Lk);
+    if (pl.S > 1) {
+        const SplitWs ws = split_ws(a.ws, a.R, pl);
+        if (!a.ws || a.ws_bytes < ws.bytes) return hipErrorInvalidValue;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(topk_split_select),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        const dim3 g((unsigned)pl.S, (unsigned)a.R);
+        hipLaunchKernelGGL(topk_split_bound, g, dim3(kSplitThreads), 0, st, a, pl, ws);
+        hipLaunchKernelGGL(topk_split_collect, g, dim3(kSplitThreads), 0, st, a, pl, ws);
+        hipLaunchKernelGGL(topk_split_select, dim3((unsigned)a.R), dim3(kThreads), lds, st, a, pl, ws);
+        return hipGetLastError();
+    }
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(row_topk_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

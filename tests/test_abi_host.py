@@ -89,10 +89,14 @@ def test_workspace_sizes_and_rejections():
     # prefill-shaped: fused kernel, no workspace
     assert ws_bytes(desc(Lq=8192, Lk=8192, topk=2048)) == (OK, 0)
     assert ws_bytes(desc(Lq=65536, Lk=65536, topk=2048)) == (OK, 0)
-    # decode-shaped: one fp32 score row per query
+    # decode-shaped: one fp32 score row per query (256-byte aligned), then the
+    # split row top-k's own workspace
     d = desc(B=32, Lq=1, Lk=200000, topk=2048)
     st, n = ws_bytes(d)
-    assert st == OK and n == 32 * 200000 * 4
+    scores_b = (32 * 200000 * 4 + 255) // 256 * 256
+    assert st == OK and n == scores_b + sa.idx_topk_workspace(32, 200000, 2048)
+    assert sa.idx_topk_workspace(32, 200000, 2048) >= 32 * 200000 * 8   # (key, index) per score
+    assert sa.idx_topk_workspace(4096, 2048, 64) == 0                     # many short rows: not split
     assert score(d) == WS
     assert score(d, ws=FAKE, wsb=n - 1) == WS
     assert score(d, ws=FAKE_ODD, wsb=n) == ALIGN
@@ -108,6 +112,12 @@ def test_topk_rejections():
     assert L.idx_topk(FAKE, None, 4, 10, 0, FAKE, None, 0, None) == SHAPE
     assert L.idx_topk(FAKE, None, 4, 10, 4096, FAKE, None, 0, None) == UNSUP
     assert L.idx_topk(None, None, 4, 10, 8, FAKE, None, 0, None) == NULL
+    # split rows need their workspace
+    need = sa.idx_topk_workspace(8, 100000, 2048)
+    assert need > 0
+    assert L.idx_topk(FAKE, None, 8, 100000, 2048, FAKE, None, 0, None) == WS
+    assert L.idx_topk(FAKE, None, 8, 100000, 2048, FAKE, FAKE, need - 1, None) == WS
+    assert L.idx_topk(FAKE, None, 8, 100000, 2048, FAKE, FAKE_ODD, need, None) == ALIGN
     assert L.idx_topk(FAKE, None, 4, 10, 8, None, None, 0, None) == NULL
     assert L.idx_topk(ctypes.c_void_p(0x10001), None, 4, 10, 8, FAKE, None, 0, None) == ALIGN
     assert L.idx_topk(FAKE, None, 0, 10, 8, FAKE, None, 0, None) == OK  # nothing to do

@@ -49,3 +49,25 @@ def test_all_equal_rows():
         s = np.full((3, 4097), v, np.float32)
         t = run(s, None, 2048)
         assert np.array_equal(t, np.tile(np.arange(2048, dtype=np.int32), (3, 1)))
+
+
+@pytest.mark.parametrize("R,Lk", [(32, 200000), (3, 70001), (100, 16384)])
+def test_split_rows(R, Lk):
+    """Few long rows: the split path (bounds per split, candidate collection, per-row select)."""
+    rng = np.random.default_rng(R + Lk)
+    s = rng.standard_normal((R, Lk)).astype(np.float32)
+    s[:, 5::997] = np.float32(2.75)          # ties near the cut
+    s[0, : Lk // 2] = np.float32(-1.0)        # one row whose top-k sits in its second half
+    pos = rng.integers(0, Lk, R).astype(np.int32)
+    pos[0] = Lk - 1
+    pos[-1] = 4096 * 3 + 17                   # ends inside a split
+    assert np.array_equal(run(s, pos, 2048), oracle.topk(s, pos, 2048))
+    assert np.array_equal(run(s, None, 2048), oracle.topk(s, None, 2048))
+    assert np.array_equal(run(s, None, 64), oracle.topk(s, None, 64))
+
+
+def test_split_rows_increasing():
+    """Sorted rows: every split's bound is loose; candidates exceed LDS and the HBM fallback runs."""
+    s = np.tile(np.arange(100000, dtype=np.float32), (4, 1))
+    s[1] = s[1][::-1]
+    assert np.array_equal(run(s, None, 2048), oracle.topk(s, None, 2048))
