@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the retention-ratio sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     ap.add_argument("--profile-only", action="store_true", help="run warmup+steps of the headline only")
     ap.add_argument("--profile", choices=["prefill", "decode", "copy"],
@@ -137,6 +138,62 @@ def decode(args, torch, sa, inputs):
 
 
 COPY_BYTES = 1 << 30   # the calibration copy moves this many bytes each way
+
+
+def retention_sweep(args, torch, sa, inputs):
+    """Layer patterns keeping 1/1, 1/2, 1/4 and 1/8 of the 16 layers Full, at the
+    32K-token stack shape: per-layer times of the indexer (Full layers only),
+    sparse MLA and the FFN stand-in, the stack time they imply for each pattern,
+    and one directly timed F,S,S,S x 4 stack for comparison."""
+    wl = inputs.WORKLOADS["stack_32k"]
+    dev = torch.device("cuda:0")
+    L, n_layers = wl.Lq, wl.layers
+    q, k, w = inputs.indexer_inputs(wl, 0, dev)
+    qa, kv = inputs.attention_inputs(wl, 0, dev)
+    W = inputs.ffn_weight(wl, 0, dev)
+    x = inputs.stack_x0(wl, dev)
+    t_cache = torch.empty(wl.B, L, wl.topk, dtype=torch.int32, device=dev)
+    out = torch.empty(wl.B, L, wl.Hq, wl.Dv, dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / math.sqrt(wl.Dqk)
+    sa.idx_cache_route("F", 0, q, k, w, t_cache)
+
+    def layer(pattern, i):
+        sa.idx_cache_route(pattern, i, q, k, w, t_cache)
+        sa.sparse_mla_attn(qa, kv, t_cache, scale, wl.Dv, out=out)
+        x1 = x.clone()
+        x1[:, :wl.Dv] += out[0].sum(dim=1)
+        return x1 + x1 @ W
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    t_idx = timed(lambda: sa.idx_cache_route("F", 0, q, k, w, t_cache))
+    t_att = timed(lambda: sa.sparse_mla_attn(qa, kv, t_cache, scale, wl.Dv, out=out))
+    t_ffn = timed(lambda: layer("FS", 1)) - t_att   # head sum, residual and FFN GEMM
+    pats = {"1/1": "F" * n_layers, "1/2": "FS" * (n_layers // 2), "1/4": "FSSS" * (n_layers // 4),
+            "1/8": "FSSSSSSS" * (n_layers // 8)}
+    res = {}
+    full = n_layers * (t_idx + t_att + t_ffn)
+    for name, pat in pats.items():
+        nf = pat.count("F")
+        stack = nf * t_idx + n_layers * (t_att + t_ffn)
+        res[name] = {"pattern": pat, "full_layers": nf, "indexer_ms": round(nf * t_idx, 3),
+                     "indexer_saved_ms": round((n_layers - nf) * t_idx, 3), "stack_ms": round(stack, 3),
+                     "speedup_vs_all_full": round(full / stack, 4)}
+    measured = timed(lambda: [layer(pats["1/4"], i) for i in range(n_layers)], n=1)
+    del q, k, w, qa, kv, out, W, x, t_cache
+    return {"workload": "stack_32k", "L": L, "layers": n_layers, "indexer_ms_per_full_layer": round(t_idx, 3),
+            "sparse_mla_ms_per_layer": round(t_att, 3), "ffn_and_residual_ms_per_layer": round(t_ffn, 3),
+            "patterns": res, "measured_FSSSx4_stack_ms": round(measured, 3),
+            "note": "stack_ms = Full layers x indexer + all layers x (sparse MLA + FFN stand-in)"}
 
 
 def profile_run(args, torch, sa, inputs):
@@ -279,6 +336,8 @@ def main():
     }
     if not args.no_decode:
         line["secondary"] = decode(args, torch, sa, inputs)
+    if not args.no_sweep:
+        line["retention_sweep"] = retention_sweep(args, torch, sa, inputs)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, inputs, torch)
     print(json.dumps(line))

@@ -163,6 +163,21 @@ idxc_status sparse_mla_attn(const idxc_mla_desc *desc, const void *q, const void
                             const int32_t *t, float sm_scale, void *out, float *lse, void *ws,
                             size_t ws_bytes, void *stream);
 
+/*
+ * Cross-layer overlap of two layers' index sets ([ITO] introduction and
+ * § "Der unsichtbare Datenstrom": adjacent layers select largely the same
+ * tokens; [PPM] § "Aandacht cachen met IndexCache"), the diagnostic behind
+ * choosing Full and Shared layers.
+ *   t_a, t_b int32 [R, topk]: rows as idx_score_topk writes them (ascending
+ *            indices, then -1 padding); rows not in that form give
+ *            unspecified counts.
+ *   counts   int32 [R]: counts[r] = number of indices >= 0 present in both
+ *            t_a[r] and t_b[r].
+ * No workspace.  1 <= topk <= 2048; pointers 4-byte aligned.
+ */
+idxc_status idx_overlap(const int32_t *t_a, const int32_t *t_b, int R, int topk, int32_t *counts,
+                        void *stream);
+
 /* Static text for a status code. */
 const char *idxc_status_str(idxc_status s);
 

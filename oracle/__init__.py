@@ -22,6 +22,7 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
   topk             pinned (brute force vs full sort and repeated argmax, closed forms)
   route            pinned (hand-worked example, invariants)
   sparse_mla       pinned (dense attention via torch SDPA on CPU, closed forms)
+  overlap          pinned (hand-worked rows, identical / disjoint / nested sets, symmetry)
   stack            parity unpinned: the way layers compose (residual add of the
                    head-summed attention output, then the seeded FFN stand-in)
                    is a reading, not something the pages fix.
@@ -237,6 +238,19 @@ def sparse_mla_dv(q, kv, t, sm_scale: float, Dv: int, rows=None, nthreads=None):
 
 
 # ---------------------------------------------------------------- helpers
+
+def overlap(t_a: np.ndarray, t_b: np.ndarray) -> np.ndarray:
+    """Per-row size of the intersection of two layers' index sets (entries < 0
+    are padding): the cross-layer overlap of [ITO] introduction / "Der
+    unsichtbare Datenstrom" and [PPM] "Aandacht cachen met IndexCache",
+    written out as a set intersection.  Works on any row order."""
+    a = np.asarray(t_a).reshape(-1, np.shape(t_a)[-1])
+    b = np.asarray(t_b).reshape(-1, np.shape(t_b)[-1])
+    out = np.empty(a.shape[0], np.int64)
+    for r in range(a.shape[0]):
+        out[r] = len(set(int(x) for x in a[r] if x >= 0) & set(int(x) for x in b[r] if x >= 0))
+    return out.reshape(np.shape(t_a)[:-1])
+
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns -> float64 (exact: shift into fp32 bits)."""

@@ -77,6 +77,8 @@ def lib():
         L.sparse_mla_attn_workspace.argtypes = [mp, szp]
         L.sparse_mla_attn.restype = i32
         L.sparse_mla_attn.argtypes = [mp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+        L.idx_overlap.restype = i32
+        L.idx_overlap.argtypes = [vp, vp, i32, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -195,6 +197,32 @@ def sparse_mla_attn_workspace(q, kv, t, Dv: int) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().sparse_mla_attn_workspace(ctypes.byref(d), ctypes.byref(n)), "sparse_mla_attn_workspace")
     return n.value
+
+
+def idx_overlap(t_a, t_b, stream=None):
+    """Per-row count of indices present in both index sets (rows ascending, -1 padded)."""
+    for name, t in (("t_a", t_a), ("t_b", t_b)):
+        _cuda_tensor(t, name)
+    if t_a.shape != t_b.shape or t_a.dtype != torch.int32 or t_b.dtype != torch.int32:
+        raise ValueError("t_a and t_b must be int32 tensors of one shape [..., topk]")
+    topk = t_a.shape[-1]
+    R = t_a.numel() // topk
+    counts = torch.empty(t_a.shape[:-1], dtype=torch.int32, device=t_a.device)
+    _check(lib().idx_overlap(_p(t_a), _p(t_b), R, topk, _p(counts), _stream(stream, t_a.device)), "idx_overlap")
+    return counts
+
+
+def overlap_matrix(ts, stream=None):
+    """Layer x layer mean overlap ratio of index sets ts[l] (each [..., topk]):
+    entry (i, j) = mean over rows of |T_i & T_j| / (valid entries of T_i)."""
+    L = len(ts)
+    valid = [(t >= 0).sum(dim=-1).clamp(min=1).to(torch.float64) for t in ts]
+    m = torch.zeros(L, L, dtype=torch.float64)
+    for i in range(L):
+        for j in range(L):
+            c = idx_overlap(ts[i], ts[j], stream=stream).to(torch.float64)
+            m[i, j] = (c / valid[i]).mean().item()
+    return m
 
 
 def sparse_mla_attn(q, kv, t, sm_scale: float, Dv: int, out=None, lse=None, ws=None, stream=None):

@@ -11,7 +11,8 @@
 //                      reduziert", section "Einfache Implementierung, enorme
 //                      Effizienzgewinne"): Full layers run idx_score_topk into
 //                      the cache buffer, Shared layers enqueue nothing;
-//   sparse_mla_attn -> sparse MLA kernel.
+//   sparse_mla_attn -> sparse MLA kernel;
+//   idx_overlap     -> per-row index-set overlap of two layers' T.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -219,6 +220,20 @@ idxc_status idx_cache_route(const char *pattern, int layer, const idxc_indexer_d
     st = run_indexer(desc, q, k, w, t_cache, nullptr, ws, path, static_cast<hipStream_t>(stream));
     if (st == IDXC_OK && computed) *computed = 1;
     return st;
+}
+
+idxc_status idx_overlap(const int32_t *t_a, const int32_t *t_b, int R, int topk, int32_t *counts, void *stream) {
+    if (R < 0 || topk < 1 || topk > kMaxTopk) return IDXC_ERR_SHAPE;
+    if (R == 0) return IDXC_OK;
+    if (!t_a || !t_b || !counts) return IDXC_ERR_NULL;
+    if (!aligned(t_a, 4) || !aligned(t_b, 4) || !aligned(counts, 4)) return IDXC_ERR_ALIGN;
+    idxc::OverlapArgs a;
+    a.t_a = t_a;
+    a.t_b = t_b;
+    a.R = R;
+    a.topk = topk;
+    a.counts = counts;
+    return from_hip(idxc::launch_overlap(a, static_cast<hipStream_t>(stream)));
 }
 
 idxc_status sparse_mla_attn_workspace(const idxc_mla_desc *desc, size_t *bytes) {

@@ -44,6 +44,15 @@ struct TopkArgs {
 size_t row_topk_ws_bytes(int R, int Lk);
 hipError_t launch_row_topk(const TopkArgs &a, hipStream_t s);
 
+// counts[r] = |{t_a[r][j] >= 0} intersected with {t_b[r][j] >= 0}|; rows
+// ascending with -1 padding.
+struct OverlapArgs {
+    const int32_t *t_a, *t_b;
+    int R, topk;
+    int32_t *counts;
+};
+hipError_t launch_overlap(const OverlapArgs &a, hipStream_t s);
+
 struct MlaArgs {
     const void *q, *kv;
     const int32_t *t;

@@ -174,3 +174,14 @@ def test_sparse_mla_rejections():
     assert mla(out=None) == NULL
     assert mla(q=FAKE_ODD) == ALIGN
     assert mla(kv=FAKE_ODD) == ALIGN
+
+
+def test_overlap_rejections():
+    L = sa.lib()
+    assert L.idx_overlap(FAKE, FAKE, 0, 8, FAKE, None) == OK        # empty: nothing enqueued
+    assert L.idx_overlap(FAKE, FAKE, -1, 8, FAKE, None) == SHAPE
+    assert L.idx_overlap(FAKE, FAKE, 4, 0, FAKE, None) == SHAPE
+    assert L.idx_overlap(FAKE, FAKE, 4, 4096, FAKE, None) == SHAPE
+    assert L.idx_overlap(None, FAKE, 4, 8, FAKE, None) == NULL
+    assert L.idx_overlap(FAKE, FAKE, 4, 8, None, None) == NULL
+    assert L.idx_overlap(ctypes.c_void_p(0x10002), FAKE, 4, 8, FAKE, None) == ALIGN
