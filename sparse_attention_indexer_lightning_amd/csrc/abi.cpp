@@ -238,14 +238,14 @@ idxc_status idx_overlap(const int32_t *t_a, const int32_t *t_b, int R, int topk,
 
 idxc_status sparse_mla_attn_workspace(const idxc_mla_desc *desc, size_t *bytes) {
     if (!desc || !bytes) return IDXC_ERR_NULL;
-    *bytes = 0;
+    const idxc_mla_desc &d = *desc;
+    const idxc::MlaWidePlan p = idxc::mla_wide_plan(d.B, d.Lq, d.Hq, d.Dqk, d.Dv, d.topk);
+    *bytes = p.ok ? p.ws_bytes : 0;
     return IDXC_OK;
 }
 
 idxc_status sparse_mla_attn(const idxc_mla_desc *desc, const void *q, const void *kv, const int32_t *t,
                             float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (!desc) return IDXC_ERR_NULL;
     const idxc_mla_desc &d = *desc;
     if (d.B < 1 || d.Lq < 1 || d.Lk < 1 || d.Hq < 1 || d.Dqk < 1 || d.Dv < 1 || d.topk < 1 || d.Dv > d.Dqk)
@@ -261,6 +261,23 @@ idxc_status sparse_mla_attn(const idxc_mla_desc *desc, const void *q, const void
     if (!q || !kv || !t || !out) return IDXC_ERR_NULL;
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(t, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)))
         return IDXC_ERR_ALIGN;
+    const idxc::MlaWidePlan plan = idxc::mla_wide_plan(d.B, d.Lq, d.Hq, d.Dqk, d.Dv, d.topk);
+    if (plan.ok) {
+        if (plan.ws_bytes > 0) {
+            if (!ws || ws_bytes < plan.ws_bytes) return IDXC_ERR_WORKSPACE;
+            if (!aligned(ws, 16)) return IDXC_ERR_ALIGN;
+        }
+        idxc::MlaWideArgs w;
+        w.q = q; w.kv = kv; w.t = t; w.out = out; w.lse = lse; w.sm_scale = sm_scale;
+        w.B = d.B; w.Lq = d.Lq; w.Lk = d.Lk; w.Hq = d.Hq; w.topk = d.topk;
+        w.nchunk = plan.nchunk; w.chunk_rows = plan.chunk_rows;
+        w.part_o = ws;
+        w.part_lse = plan.ws_bytes > 0
+                         ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) +
+                                                     (size_t)d.B * d.Lq * d.Hq * plan.nchunk * d.Dv * 2)
+                         : nullptr;
+        return from_hip(idxc::launch_sparse_mla_wide(w, static_cast<hipStream_t>(stream)));
+    }
     idxc::MlaArgs a;
     a.q = q; a.kv = kv; a.t = t; a.out = out; a.lse = lse; a.sm_scale = sm_scale;
     a.B = d.B; a.Lq = d.Lq; a.Lk = d.Lk; a.Hq = d.Hq; a.Dqk = d.Dqk; a.Dv = d.Dv; a.topk = d.topk;

@@ -63,4 +63,29 @@ struct MlaArgs {
 };
 hipError_t launch_sparse_mla(const MlaArgs &a, hipStream_t s);
 
+// Sparse MLA with 64 heads of a query per workgroup (Dqk 576, Dv 512,
+// Hq a multiple of 64).  With nchunk > 1 each query's index set is split
+// into chunks of chunk_rows positions; every chunk writes its normalised
+// output (bf16 [B*Lq][nchunk][Hq][512]) and log2-sum-exp (fp32
+// [B*Lq][nchunk][Hq]) to part_o / part_lse and a merge kernel combines them.
+struct MlaWideArgs {
+    const void *q, *kv;
+    const int32_t *t;
+    void *out;
+    float *lse;
+    float sm_scale;
+    int B, Lq, Lk, Hq, topk;
+    int nchunk, chunk_rows;
+    void *part_o;
+    float *part_lse;
+};
+struct MlaWidePlan {
+    bool ok;            // the shape is served by the wide kernel
+    int nchunk, chunk_rows;
+    size_t ws_bytes;    // partial outputs, 0 when nchunk == 1
+};
+constexpr int kMlaTargetWorkgroups = 256;   // one per compute unit of MI355X
+MlaWidePlan mla_wide_plan(int B, int Lq, int Hq, int Dqk, int Dv, int topk);
+hipError_t launch_sparse_mla_wide(const MlaWideArgs &a, hipStream_t s);
+
 }  // namespace idxc

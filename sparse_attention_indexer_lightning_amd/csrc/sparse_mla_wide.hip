@@ -1,0 +1,539 @@
+// sparse_mla_wide.hip -- sparse MLA attention with 64 heads of a query per
+// workgroup.
+//
+// itoverdose.com, "IndexCache: Wie DeepSeek O(NL²)-Kosten in Sparse Attention
+// um 75% reduziert": the introduction (attention runs only over the k selected
+// tokens) and section "Wie der Indexer funktioniert und warum MLA entscheidend
+// ist" (every head reads one compressed latent row per token).  In the absorbed
+// form all heads share the row: keys are the whole row (576 columns), values
+// its first 512 columns.
+//
+// Each gathered row is used by 64 heads at once, so the rows of a query move
+// from L2 into compute units Hq/64 times instead of once per 16-head group.
+// When there are too few queries to fill the chip (decode), each query's
+// index set is split into chunks that run as separate workgroups, and a second
+// kernel merges their normalised partial outputs by log-sum-exp weights.
+//
+// Workgroup: one query, 64 heads, one chunk of the index set; 4 wavefronts
+// in two roles that run one tile apart:
+//  * Rows are consumed in tiles of 32.  Tiles are copied straight from HBM
+//    into a ring of four LDS slots with LDS-direct 16-byte loads, two tiles
+//    ahead; the index values that drive the copies are themselves copied
+//    into a small LDS ring four tiles ahead.  All wavefronts copy.
+//  * Producers (wavefronts 0, 1; heads 32p..32p+31): S^T = K Q^T for the 32
+//    rows of tile s on 32x32x16 bf16 MFMA, query fragments held in registers
+//    for the whole sweep; the softmax probabilities go to LDS in bf16.  Each
+//    head's reference is raised lazily, only when a tile's maximum exceeds it
+//    by more than kSlack (log2 units), and the producer that owns the head
+//    publishes the rescale factor with the probabilities.
+//  * Consumers (wavefronts 2, 3; output columns 256c..256c+255 of all 64
+//    heads): O^T += V^T P^T for tile s-1, V^T read with transposing LDS loads;
+//    a published rescale is applied before the tile it belongs to.
+//  * One workgroup barrier per tile.  The two roles are separate code paths,
+//    so the query fragments (producers) and the output accumulators
+//    (consumers) never need registers in the same wavefront.
+#include <algorithm>
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace idxc {
+namespace {
+namespace wide {
+
+constexpr int DQK = 576, DV = 512;
+constexpr int HW = 64;                        // heads per workgroup
+constexpr int RT = 32;                        // rows per tile
+constexpr int ROWB = DQK * 2;                 // bytes per latent row
+constexpr int OCTETS = ROWB / 128;            // 128-byte lines per row
+constexpr int OCT_BYTES = RT * 128;           // one line of every row of a tile
+constexpr int SLOT = OCTETS * OCT_BYTES;      // bytes per tile
+constexpr int WAVES = 4;
+constexpr int KS = DQK / 16;                  // logit k-steps
+constexpr int RING = 8;                       // index ring, in tiles
+constexpr int PB = HW * RT * 2;               // probability tile, bf16 [head][row]
+constexpr float kSlack = 8.f;
+static_assert(ROWB % 128 == 0, "rows are whole 128-byte lines");
+static_assert(RT == 8 * WAVES, "each wavefront copies one 8-row group");
+static_assert(HW == 64 && DV == 512, "two producers of 32 heads, two consumers of 256 columns");
+
+// Slot layout: line-major [line q][row r][position], where 16-byte piece
+// 8q + p of row r sits at position (p + f(r)) mod 8.  f makes the two LDS
+// read shapes conflict-free: 16 consecutive rows x one piece (logit
+// operand), and 4 consecutive rows x 4 aligned pieces (transposed V reads).
+__device__ __forceinline__ int rot(int r) { return ((r >> 2) & 3) + 4 * ((r >> 1) & 1); }
+__device__ __forceinline__ int pos_of(int p, int r) { return (p + rot(r)) & 7; }
+__device__ __forceinline__ int piece_at(int pos, int r) { return (pos - rot(r)) & 7; }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ v4s lds_read_tr16(const lds_u8 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+}
+__device__ __forceinline__ v4i lds_read_b128(const lds_u8 *p) { return *(const __attribute__((address_space(3))) v4i *)p; }
+__device__ __forceinline__ void lds_write_b64(lds_u8 *p, v2i v) { *(__attribute__((address_space(3))) v2i *)p = v; }
+
+// D(32x32, fp32) = A(32x16, bf16) * B(16x32, bf16) + C.  Lane l supplies
+// row/column l%32 and k-values 8*(l/32)..+7; register r of the result holds
+// D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(const v8bf &a, const v8bf &b, const v16f &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// s_waitcnt immediate for vmcnt(n) with the other counters unconstrained
+// (vmcnt is split over bits 3:0 and 15:14).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Workgroup barrier ordering LDS accesses only: the LDS-direct copies still
+// in flight are waited for with explicit vmcnt bounds, not here.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One 8-row group rg of a tile: load Q moves line Q of the group's rows
+// (lane l: row 8rg + l/8, position l%8).  The immediate offset 128Q applies
+// to the global and to the LDS address, so the LDS base is lowered by it.
+template <int Q>
+__device__ __forceinline__ void fill_group(const unsigned char *src, lds_u8 *slot, int rg) {
+    if constexpr (Q < OCTETS) {
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(slot + (OCT_BYTES - 128) * Q + 1024 * rg),
+                                         16, 128 * Q, 0);
+        fill_group<Q + 1>(src, slot, rg);
+    }
+}
+
+__device__ __forceinline__ float swap32_max(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float swap32_sum(float v) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// Keeps a per-step copy of an LDS offset opaque, so that the compiler adds
+// the slot base inside the step instead of holding base + offset for every
+// slot in registers across the loop.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Keeps an accumulator block in accumulation registers at this point (an
+// empty asm with an AGPR operand): the output accumulators fill the AGPR
+// file, and this stops the compiler from holding whole sets of them in
+// VGPRs around the rare rescale and the final read-out.
+__device__ __forceinline__ void pin_acc(v16f &x) { asm volatile("" : "+a"(x)); }
+
+struct Smem {
+    unsigned char ptile[2][PB];               // [tile parity] bf16 [head][4 chunks of 8 rows]
+    int ring[RING][RT];                       // index values of tiles t % RING
+    float alpha[2][HW];                       // [tile parity] rescale factor per head
+    int flag[2][2];                           // [tile parity][producer] some head was rescaled
+    float lsum[HW], mref[HW];
+};
+
+__global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideArgs a) {
+    __shared__ __align__(16) unsigned char slot0[SLOT];
+    __shared__ __align__(16) unsigned char slot1[SLOT];
+    __shared__ __align__(16) unsigned char slot2[SLOT];
+    __shared__ __align__(16) unsigned char slot3[SLOT];
+    __shared__ __align__(16) Smem sm;
+
+    // workgroup -> (query, head block, chunk); the chunks and head blocks of
+    // one query, and runs of neighbouring queries, share an XCD and its L2
+    const int total = (int)gridDim.x;
+    int id = (int)blockIdx.x;
+    if (total % 8 == 0) id = (id % 8) * (total / 8) + id / 8;
+    const int chunk = id % a.nchunk;
+    const int qb = id / a.nchunk;                 // query * head blocks + head block
+    const int nhb = a.Hq / HW;
+    const int qrow = qb / nhb, h0 = (qb % nhb) * HW;
+    const int b = qrow / a.Lq;
+    const int cs = chunk * a.chunk_rows;          // first position of the chunk
+    const int clen = min(a.chunk_rows, a.topk - cs);
+    const int ntiles = (clen + RT - 1) / RT;
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int n = lane & 31, hh = lane >> 5;
+    const unsigned char *kvb = static_cast<const unsigned char *>(a.kv) + (size_t)b * a.Lk * ROWB;
+    const int32_t *trow = a.t + (size_t)qrow * a.topk;
+    auto SL = [&](auto I) -> lds_u8 * {
+        constexpr int i = decltype(I)::value & 3;
+        if constexpr (i == 0) return (lds_u8 *)slot0;
+        else if constexpr (i == 1) return (lds_u8 *)slot1;
+        else if constexpr (i == 2) return (lds_u8 *)slot2;
+        else return (lds_u8 *)slot3;
+    };
+
+    // index ring: tiles 0..3 now, tile s+4 at the end of step s
+    if (tid < 4 * RT) sm.ring[tid / RT][tid % RT] = trow[min(cs + tid, a.topk - 1)];
+    lds_barrier();
+
+    // Copies are issued by the two consumer wavefronts only (consumer c
+    // copies row groups 2c and 2c+1 of every tile), so that the producers,
+    // which set the pace, spend no issue slots on them.  Lane l of a group
+    // copy moves position l%8 of row 8rg + l/8.
+    auto copy_group = [&](lds_u8 *slot, int t, int ix, int rg) {
+        const int row = 8 * rg + (lane >> 3);
+        const bool ok = RT * t + row < clen && ix >= 0 && ix < a.Lk;
+        fill_group<0>(kvb + (size_t)(uint32_t)(ok ? ix : 0) * ROWB + 16 * piece_at(lane & 7, row), slot, rg);
+    };
+    // steps 0..ntiles in groups of four (slot parity is a template argument;
+    // no conditional step inside the loop keeps the compiler's tracking of
+    // the copies exact), the remainder after the loop
+    auto run = [&](auto &&step) {
+        int s = 0;
+        for (; s + 3 <= ntiles; s += 4) {
+            step(std::integral_constant<int, 0>{}, s);
+            step(std::integral_constant<int, 1>{}, s + 1);
+            step(std::integral_constant<int, 2>{}, s + 2);
+            step(std::integral_constant<int, 3>{}, s + 3);
+        }
+        if (s <= ntiles) step(std::integral_constant<int, 0>{}, s);
+        if (s + 1 <= ntiles) step(std::integral_constant<int, 1>{}, s + 1);
+        if (s + 2 <= ntiles) step(std::integral_constant<int, 2>{}, s + 2);
+    };
+
+    if (wave < 2) {
+        // ---------------- producer: logits and probabilities of heads 32p..32p+31
+        const int p = wave;
+        const int H = 32 * p + n;                 // head (within the block) of this lane
+        const float sl2 = a.sm_scale * 1.4426950408889634f;
+        v4i qf[KS];                               // B operand: head h0 + H, piece 2c + hh
+        {
+            const v4i *qh = reinterpret_cast<const v4i *>(static_cast<const unsigned char *>(a.q) +
+                                                          ((size_t)qrow * a.Hq + h0 + H) * ROWB);
+#pragma unroll
+            for (int c = 0; c < KS; ++c) qf[c] = qh[2 * c + hh];
+        }
+        // A operand: row n of the tile, piece 2c + hh = line c/4, piece 2(c%4) + hh
+        int kb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) kb[k] = 128 * n + 16 * pos_of(2 * k + hh, n);
+        float m_ref = -INFINITY, l_lane = 0.f;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // query fragments
+        lds_barrier();   // tile 0 landed (consumers' copies)
+        int ix_mask = sm.ring[0][n];
+        auto step = [&](auto PI_, int s) {
+            constexpr int PI = decltype(PI_)::value;
+            lds_u8 *cur = SL(std::integral_constant<int, PI>{});
+            const int ix_mask_next = sm.ring[(s + 1) & (RING - 1)][n];
+            if (s < ntiles) {
+                int kbs[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) kbs[k] = opaque(kb[k]);
+                // software pipeline over groups of four k-steps: the reads of
+                // group g+1 are in flight while group g runs on the MFMA unit
+                v16f sacc = v16f{};
+                v4i kf[2][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) kf[0][i] = lds_read_b128(cur + kbs[i] + OCT_BYTES * 0);
+#pragma unroll
+                for (int g = 0; g < KS / 4; ++g) {
+                    if (g + 1 < KS / 4) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) kf[(g + 1) & 1][i] = lds_read_b128(cur + kbs[i] + OCT_BYTES * (g + 1));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sacc = mfma_bf16_32x32x16(__builtin_bit_cast(v8bf, kf[g & 1][i]), __builtin_bit_cast(v8bf, qf[4 * g + i]), sacc);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // rows of this lane: 8i + 4hh + j for register 4i + j; logits
+                // stay unscaled (z * sl2 is formed inside the exponent)
+                const bool vrow = RT * s + n < clen && ix_mask >= 0 && ix_mask < a.Lk;
+                const uint64_t vball = ballot(vrow && hh == 0);
+                const bool all_valid = (uint32_t)vball == 0xFFFFFFFFu;
+                float lm = -INFINITY;
+                if (all_valid) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) lm = fmaxf(lm, sacc[r]);
+                } else {
+                    const uint32_t vmask = (uint32_t)vball >> (4 * hh);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        sacc[r] = ((vmask >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] : -INFINITY;
+                        lm = fmaxf(lm, sacc[r]);
+                    }
+                }
+                lm = swap32_max(lm) * sl2;   // sl2 > 0: the maximum of the scaled logits
+                const float m_new = lm > m_ref + kSlack ? lm : m_ref;
+                const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                const int par = s & 1;
+                if (hh == 0) sm.alpha[par][H] = alpha;
+                const bool raised = ballot(m_new != m_ref) != 0;
+                if (lane == 0) sm.flag[par][p] = raised ? 1 : 0;
+                float ps = 0.f;
+                lds_u8 *pt = (lds_u8 *)sm.ptile[par] + 64 * H + 8 * hh;
+                // exp2(-inf) = 0 takes care of masked rows whenever m_new is
+                // finite; m_new = -inf means no valid row so far (all zero)
+                const float mneg = m_new == -INFINITY ? 0.f : -m_new;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float pv[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], sl2, mneg));
+                        ps += pv[j];
+                    }
+                    v2i w2;
+                    w2[0] = (int)pack_bf16(pv[0], pv[1]);
+                    w2[1] = (int)pack_bf16(pv[2], pv[3]);
+                    lds_write_b64(pt + 16 * ((i + (H >> 2)) & 3), w2);
+                }
+                l_lane = l_lane * alpha + ps;
+                m_ref = m_new;
+            }
+            lds_barrier();   // P of tile s visible; tile s+1 landed (consumers' copies)
+            ix_mask = ix_mask_next;
+        };
+        run(step);
+        const float l_head = swap32_sum(l_lane);
+        if (hh == 0) {
+            sm.lsum[H] = l_head;
+            sm.mref[H] = m_ref;
+        }
+        lds_barrier();   // statistics visible
+        lds_barrier();   // consumers staged the output
+    } else {
+        // ---------------- consumer: output columns 256c..256c+255 of all 64 heads
+        const int c = wave - 2;
+        // transposed V reads: lane (G = lane/16, j = (lane/4)%4, cc = lane%4) ->
+        // row 8(G/2) + 4t + j, columns 256c + 32mb + 16(G%2) + 4cc..+3 = line
+        // 4c + mb/2, piece 4(mb%2) + 2(G%2) + cc/2, byte 8(cc%2)
+        int vb[2][2];
+        {
+            const int G = lane >> 4, j = (lane >> 2) & 3, cc = lane & 3;
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int r = 8 * (G >> 1) + 4 * t + j;
+                    vb[m2][t] = OCT_BYTES * 4 * c + 128 * r + 16 * pos_of(4 * m2 + 2 * (G & 1) + (cc >> 1), r) + 8 * (cc & 1);
+                }
+        }
+        // B operand of k-step cp: head 32nb + n, rows 16cp + 8hh..+7 = chunk
+        // q = 2cp + hh, stored at 16((q + H/4) mod 4)
+        int pbase[2];
+#pragma unroll
+        for (int cp = 0; cp < 2; ++cp) pbase[cp] = 64 * n + 16 * ((2 * cp + hh + (n >> 2)) & 3);
+        v16f o[8][2];
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) o[mb][nb] = v16f{};
+        // index values of tile t for rows 16c..16c+15 (lane l holds row
+        // 16c + l%16), loaded by every lane so that each step issues the same
+        // number of vector-memory operations whatever the lane mask
+        auto load_index = [&](int t) -> int { return trow[min(cs + RT * t + 16 * c + (lane & 15), a.topk - 1)]; };
+        const int crow0 = 16 * c + (lane >> 3), crow1 = crow0 + 8;   // copy rows of groups 2c, 2c+1
+        int pend = load_index(4);
+        copy_group(SL(std::integral_constant<int, 0>{}), 0, sm.ring[0][crow0], 2 * c);
+        copy_group(SL(std::integral_constant<int, 0>{}), 0, sm.ring[0][crow1], 2 * c + 1);
+        copy_group(SL(std::integral_constant<int, 1>{}), 1, sm.ring[1][crow0], 2 * c);
+        copy_group(SL(std::integral_constant<int, 1>{}), 1, sm.ring[1][crow1], 2 * c + 1);
+        int ix0 = sm.ring[2][crow0], ix1 = sm.ring[2][crow1];
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OCTETS));   // the index load and tile 0 landed
+        lds_barrier();
+        // step s starts with the load of the indices of tile s+5 and the
+        // copy of tile s+2 (19 vector-memory operations); it ends by waiting
+        // for tile s+1 and the indices of tile s+4, which then go to the ring
+        auto step = [&](auto PI_, int s) {
+            constexpr int PI = decltype(PI_)::value;
+            lds_u8 *prv = SL(std::integral_constant<int, PI + 3>{});
+            lds_u8 *nx2 = SL(std::integral_constant<int, PI + 2>{});   // held tile s-2, consumed before the last barrier
+            const int pend_next = load_index(s + 5);
+            copy_group(nx2, s + 2, ix0, 2 * c);
+            copy_group(nx2, s + 2, ix1, 2 * c + 1);
+            const int ix0_next = sm.ring[(s + 3) & (RING - 1)][crow0];
+            const int ix1_next = sm.ring[(s + 3) & (RING - 1)][crow1];
+            if (s >= 1) {
+                const int par = (s - 1) & 1;
+                if (sm.flag[par][0] | sm.flag[par][1]) {
+                    // a reference of tile s-1 was raised: rescale tiles 0..s-2
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) {
+                        const float al = sm.alpha[par][32 * nb + n];
+#pragma unroll
+                        for (int mb = 0; mb < 8; ++mb) {
+                            pin_acc(o[mb][nb]);
+                            o[mb][nb] *= al;
+                            pin_acc(o[mb][nb]);
+                        }
+                    }
+                }
+                int vbs[2][2], pbs[2];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) vbs[m2][t] = opaque(vb[m2][t]);
+#pragma unroll
+                for (int cp = 0; cp < 2; ++cp) pbs[cp] = opaque(pbase[cp]);
+                // software pipeline over the 16 (k-step, output block) stages:
+                // the V^T reads of stage i+2 and the P^T reads of the next
+                // k-step are in flight while stage i runs on the MFMA unit
+                auto read_v = [&](int i) -> v8bf {
+                    const int cp = i >> 3, mb = i & 7;
+                    const v4s lo = lds_read_tr16(prv + vbs[mb & 1][0] + OCT_BYTES * (mb >> 1) + 2048 * cp);
+                    const v4s hi = lds_read_tr16(prv + vbs[mb & 1][1] + OCT_BYTES * (mb >> 1) + 2048 * cp);
+                    return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                };
+                auto read_p = [&](int cp, int nb) -> v8bf {
+                    return __builtin_bit_cast(v8bf, lds_read_b128((lds_u8 *)sm.ptile[par] + pbs[cp] + 2048 * nb));
+                };
+                v8bf pb[2][2], va[3];
+                pb[0][0] = read_p(0, 0);
+                pb[0][1] = read_p(0, 1);
+                va[0] = read_v(0);
+                va[1] = read_v(1);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i + 2 < 16) va[(i + 2) % 3] = read_v(i + 2);
+                    if (i == 4) {
+                        pb[1][0] = read_p(1, 0);
+                        pb[1][1] = read_p(1, 1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int cp = i >> 3, mb = i & 7;
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma_bf16_32x32x16(va[i % 3], pb[cp][nb], o[mb][nb]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OCTETS + 1));
+            if (lane < 16) sm.ring[(s + 4) & (RING - 1)][16 * c + lane] = pend;
+            lds_barrier();
+            pend = pend_next;
+            ix0 = ix0_next;
+            ix1 = ix1_next;
+        };
+        run(step);
+        // the copies past the last tile may still be in flight: let them
+        // land before the slots are reused and the LDS is released
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();   // producers' statistics visible
+        // normalised output in bf16, staged through the free slots as
+        // [head][512 columns] (head H in slot H/32, 16-byte unit u of its row
+        // at u ^ (H % 32)), then written with whole-row stores
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const float L = sm.lsum[32 * nb + n];
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            lds_u8 *stg = nb == 0 ? (lds_u8 *)slot0 : (lds_u8 *)slot1;
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) {
+                pin_acc(o[mb][nb]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int col = 256 * c + 32 * mb + 8 * i + 4 * hh;   // 4 columns, 8 bytes
+                    v2i w2;
+                    w2[0] = (int)pack_bf16(o[mb][nb][4 * i] * inv, o[mb][nb][4 * i + 1] * inv);
+                    w2[1] = (int)pack_bf16(o[mb][nb][4 * i + 2] * inv, o[mb][nb][4 * i + 3] * inv);
+                    lds_write_b64(stg + 1024 * n + 16 * ((col >> 3) ^ n) + 8 * ((col >> 2) & 1), w2);
+                }
+            }
+        }
+        lds_barrier();   // output staged
+    }
+
+    unsigned char *dst;
+    if (a.nchunk == 1)
+        dst = static_cast<unsigned char *>(a.out) + ((size_t)qrow * a.Hq + h0) * DV * 2;
+    else
+        dst = static_cast<unsigned char *>(a.part_o) + (((size_t)qrow * a.nchunk + chunk) * a.Hq + h0) * DV * 2;
+    {
+        const int u = tid & 63;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            lds_u8 *stg = nb == 0 ? (lds_u8 *)slot0 : (lds_u8 *)slot1;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int hl = (tid >> 6) + 4 * k;   // head 32nb + hl
+                const v4i v = lds_read_b128(stg + 1024 * hl + 16 * (u ^ hl));
+                *reinterpret_cast<v4i *>(dst + (size_t)(32 * nb + hl) * DV * 2 + 16 * u) = v;
+            }
+        }
+    }
+    if (tid < HW) {
+        const float L = sm.lsum[tid];
+        const float lse2 = L > 0.f ? sm.mref[tid] + __log2f(L) : -INFINITY;
+        if (a.nchunk == 1) {
+            if (a.lse) a.lse[(size_t)qrow * a.Hq + h0 + tid] = lse2 * 0.6931471805599453f;
+        } else {
+            a.part_lse[((size_t)qrow * a.nchunk + chunk) * a.Hq + h0 + tid] = lse2;
+        }
+    }
+}
+
+// Merge of the chunk partials of one (query, head) per wavefront: weights
+// 2^(lse_c - max), output = weighted mean of the normalised partials.
+__global__ __launch_bounds__(256) void sparse_mla_merge_kernel(MlaWideArgs a) {
+    const int w = (int)(blockIdx.x * 4 + threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    if (w >= a.B * a.Lq * a.Hq) return;
+    const int qrow = w / a.Hq, h = w % a.Hq;
+    const float *pl = a.part_lse + (size_t)qrow * a.nchunk * a.Hq + h;
+    float mx = -INFINITY;
+    for (int c = 0; c < a.nchunk; ++c) mx = fmaxf(mx, pl[(size_t)c * a.Hq]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (mx != -INFINITY) {
+        for (int c = 0; c < a.nchunk; ++c) {
+            const float lc = pl[(size_t)c * a.Hq];
+            if (lc == -INFINITY) continue;
+            const float wc = __builtin_amdgcn_exp2f(lc - mx);
+            wsum += wc;
+            const v4i v = *reinterpret_cast<const v4i *>(static_cast<const unsigned char *>(a.part_o) +
+                                                         (((size_t)qrow * a.nchunk + c) * a.Hq + h) * DV * 2 + 16 * lane);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc[2 * k] += wc * __uint_as_float((uint32_t)v[k] << 16);
+                acc[2 * k + 1] += wc * __uint_as_float((uint32_t)v[k] & 0xFFFF0000u);
+            }
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    v4i o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = (int)pack_bf16(acc[2 * k] * inv, acc[2 * k + 1] * inv);
+    *reinterpret_cast<v4i *>(static_cast<unsigned char *>(a.out) + ((size_t)qrow * a.Hq + h) * DV * 2 + 16 * lane) = o;
+    if (a.lse && lane == 0)
+        a.lse[(size_t)qrow * a.Hq + h] = wsum > 0.f ? (mx + __log2f(wsum)) * 0.6931471805599453f : -INFINITY;
+}
+
+}  // namespace wide
+}  // namespace
+
+MlaWidePlan mla_wide_plan(int B, int Lq, int Hq, int Dqk, int Dv, int topk) {
+    MlaWidePlan p{};
+    if (Dqk != wide::DQK || Dv != wide::DV || Hq % wide::HW != 0 || topk < 1) return p;
+    const long long nq = (long long)B * Lq * (Hq / wide::HW);
+    const int ntiles = (topk + wide::RT - 1) / wide::RT;
+    // enough workgroups for the 256 compute units, at least 4 tiles each
+    long long want = nq >= kMlaTargetWorkgroups ? 1 : (kMlaTargetWorkgroups + nq - 1) / nq;
+    want = std::min<long long>(want, std::max(1, ntiles / 4));
+    const int tiles_per = (int)((ntiles + want - 1) / want);
+    p.chunk_rows = tiles_per * wide::RT;
+    p.nchunk = (topk + p.chunk_rows - 1) / p.chunk_rows;
+    p.ws_bytes = p.nchunk > 1 ? (size_t)B * Lq * Hq * p.nchunk * (wide::DV * 2 + 4) : 0;
+    p.ok = true;
+    return p;
+}
+
+hipError_t launch_sparse_mla_wide(const MlaWideArgs &a, hipStream_t st) {
+    const unsigned nwg = (unsigned)((size_t)a.B * a.Lq * (a.Hq / wide::HW) * a.nchunk);
+    hipLaunchKernelGGL(wide::sparse_mla_wide_kernel, dim3(nwg), dim3(wide::WAVES * kWave), 0, st, a);
+    if (a.nchunk > 1) {
+        const unsigned nm = (unsigned)(((size_t)a.B * a.Lq * a.Hq + 3) / 4);
+        hipLaunchKernelGGL(wide::sparse_mla_merge_kernel, dim3(nm), dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace idxc

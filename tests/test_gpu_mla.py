@@ -34,6 +34,8 @@ def run_and_compare(B, Lq, Lk, Hq, Dqk, Dv, k, t_kind="random", seed=0):
             elif t_kind == "full":
                 n = min(k, Lk)
                 t[b, i, :n] = rng.choice(Lk, size=n, replace=False)
+            elif t_kind == "dup":
+                t[b, i] = rng.integers(0, min(Lk, k // 4 + 1), size=k)
     tt = torch.from_numpy(t).to(DEV)
     scale = 1.0 / math.sqrt(Dqk)
     lse = torch.empty(B, Lq, Hq, dtype=torch.float32, device=DEV)
@@ -66,3 +68,30 @@ def test_mla_full_index_sets():
 
 def test_empty_index_set():
     run_and_compare(1, 2, 100, 16, 576, 512, 64, t_kind="empty")
+
+
+# Shapes served by the 64-heads-per-workgroup kernel (Hq a multiple of 64):
+# few queries split each index set into chunks merged by a second kernel,
+# many queries run one workgroup per (query, 64 heads).
+@pytest.mark.parametrize("B,Lq,Hq,k", [
+    (1, 3, 64, 2048),     # 16 chunks of 128 rows
+    (1, 3, 64, 1000),     # 8 chunks, the last one ragged
+    (1, 1, 192, 300),     # three head blocks, ragged tiles
+    (2, 1, 128, 37),      # one partial tile
+    (2, 128, 64, 96),     # one chunk per query, 256 workgroups
+])
+def test_mla_wide(B, Lq, Hq, k):
+    run_and_compare(B, Lq, 4000, Hq, 576, 512, k, seed=B * 1000 + Lq + Hq + k)
+
+
+def test_mla_wide_full_index_sets():
+    run_and_compare(1, 2, 2100, 64, 576, 512, 2048, t_kind="full", seed=11)
+
+
+def test_mla_wide_repeated_indices():
+    # each occurrence of an index is one more term of the softmax
+    run_and_compare(1, 2, 3000, 64, 576, 512, 512, t_kind="dup", seed=12)
+
+
+def test_mla_wide_empty_index_set():
+    run_and_compare(2, 2, 100, 64, 576, 512, 256, t_kind="empty")
