@@ -40,6 +40,8 @@
 // when any row must compact, every row past half its slack compacts too, so
 // waves stall on each other's compactions far less often.  At the end the
 // exact selection leaves min(k, p+1) entries, already in ascending order.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -177,15 +179,9 @@ __device__ __forceinline__ float epi32(const v16f &a0, const v16f &a1, const Q32
     return (c[0] + c[1]) + (c[2] + c[3]);
 }
 
-// Scores of 64 keys for one query.  kb(cf, st) returns the lane's 32-byte B
-// piece: key 32cf + l%32, d = 64st + 32(l/32) .. +31.  Lane l gets key l.
-template <typename KB32>
-__device__ __forceinline__ float score64_mfma32(const Q32 &Q, KB32 kb) {
-    v8i B[2][2];
-#pragma unroll
-    for (int cf = 0; cf < 2; ++cf)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) B[cf][st] = kb(cf, st);
+// Scores of 64 keys for one query from the lane's B pieces B[cf][st]:
+// key 32cf + l%32, d = 64st + 32(l/32) .. +31.  Lane l gets key l.
+__device__ __forceinline__ float score64_mfma32_b(const Q32 &Q, const v8i (&B)[2][2]) {
     const v16f z = {};
     v16f acc[2][2];   // [rf][cf]
 #pragma unroll
@@ -208,6 +204,17 @@ __device__ __forceinline__ float score64_mfma32(const Q32 &Q, KB32 kb) {
     // lanes 0-31 hold column fragment 0 of their head half, lanes 32-63 the other half
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// As score64_mfma32_b, with kb(cf, st) returning the lane's 32-byte B piece.
+template <typename KB32>
+__device__ __forceinline__ float score64_mfma32(const Q32 &Q, KB32 kb) {
+    v8i B[2][2];
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) B[cf][st] = kb(cf, st);
+    return score64_mfma32_b(Q, B);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -897,6 +904,7 @@ struct ScoreParams {
 };
 
 constexpr int kDecodeWaves = 4;
+constexpr int kComputeUnits = 256;   // MI355X
 
 // 64 heads of one query against a contiguous key range; B operands are read
 // straight from HBM (each key is used by exactly one query row here).
@@ -928,18 +936,51 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
         }
     }
     const unsigned char *kb = p.k + (size_t)b * p.Lk * S::ROWB;
+    if constexpr (kMfma32) {
+        // the keys of the next block are loaded while the current one is
+        // scored (two register buffers used in turn, so that no loaded value
+        // is moved before use): up to two blocks (16 KB) of loads in flight
+        // per wavefront.  The prefetch is unconditional, clamped to the last
+        // key, so that every iteration issues the same loads and the
+        // compiler's waits stay exact.
+        constexpr int STRIDE = kDecodeWaves * KB;
+        auto load_block = [&](v8i (&B)[2][2], int base) {
+#pragma unroll
+            for (int cf = 0; cf < 2; ++cf) {
+                const int key = min(base + 32 * cf + (lane & 31), p.Lk - 1);
+#pragma unroll
+                for (int st = 0; st < 2; ++st) B[cf][st] = load32(kb + (size_t)key * S::ROWB + 64 * st + 32 * (lane >> 5));
+            }
+        };
+        auto score_block = [&](const v8i (&B)[2][2], int base) {
+            const float sc = score64_mfma32_b(Q32f, B);
+            const int s = base + lane;
+            if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
+        };
+        const int last = min(s1, pos + 1);        // keys at or before the query position
+        int base = s0 + wave * KB;
+        v8i B0[2][2], B1[2][2];
+        if (base < last) load_block(B0, base);
+        for (; base < last; base += 2 * STRIDE) {
+            load_block(B1, base + STRIDE);
+            score_block(B0, base);
+            if (base + STRIDE >= last) {
+                base += STRIDE;
+                break;
+            }
+            load_block(B0, base + 2 * STRIDE);
+            score_block(B1, base + STRIDE);
+        }
+        for (; base < s1; base += STRIDE) {
+            const int s = base + lane;
+            if (s < s1) out[s] = -INFINITY;
+        }
+        return;
+    }
     for (int base = s0 + wave * KB; base < s1; base += kDecodeWaves * KB) {
         const int s = base + lane;
         if (base > pos) {
             if (s < s1) out[s] = -INFINITY;
-            continue;
-        }
-        if constexpr (kMfma32) {
-            const float sc = score64_mfma32(Q32f, [&](int cf, int st) {
-                const int key = min(base + 32 * cf + (lane & 31), p.Lk - 1);
-                return load32(kb + (size_t)key * S::ROWB + 64 * st + 32 * (lane >> 5));
-            });
-            if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
             continue;
         }
         Frag<E, D> Bf[4];
@@ -1057,8 +1098,14 @@ hipError_t launch_decode_d(const IndexerArgs &a, hipStream_t st) {
     p.w = a.w;
     p.scores = a.scores;
     p.B = a.B; p.Lq = a.Lq; p.Lk = a.Lk;
-    p.split = 4096;
     p.w_enc = a.w_enc;
+    // one round of workgroups: two per compute unit (the kernel's register
+    // use allows two resident), each a contiguous key range of a multiple of
+    // 256 keys (one 64-key block per wavefront and iteration)
+    const int rows = a.B * a.Lq;
+    const int max_split = (a.Lk + 255) / 256;
+    const int want = std::max(1, std::min(max_split, (2 * kComputeUnits + rows - 1) / rows));
+    p.split = ((a.Lk + want - 1) / want + 255) / 256 * 256;
     const int nsplit = (a.Lk + p.split - 1) / p.split;
     hipLaunchKernelGGL((decode_scores_kernel<E, D>), dim3((unsigned)nsplit, (unsigned)(a.B * a.Lq)),
                        dim3(kDecodeWaves * kWave), 0, st, p);
