@@ -6,11 +6,13 @@
  * Sources (web pages, cited by title and section):
  *   [ITO] itoverdose.com, "IndexCache: Wie DeepSeek O(NL²)-Kosten in Sparse
  *         Attention um 75% reduziert"
- *   [PPM] parapluman.nl, Dutch article on IndexCache, sections "Het DSA-knelpunt"
- *         and "Aandacht cachen met IndexCache"
+ *   [PPM] parapluman.nl, Dutch article on IndexCache, sections "Het DSA-knelpunt",
+ *         "Aandacht cachen met IndexCache", "Real-world versnellingen op
+ *         productiemodellen" and "IndexCache in productie brengen"
  *   [AIB] aiboss88.com, "IndexCache - 清華大学とZhipuが共同開発した、
  *         スパースアテンション高速化技術。 - AiBoss", sections "IndexCacheの主な機能"
  *         and the comparison table "IndexCacheと類似の競合製品との比較"
+ *   [SAI] setupai.cc, "IndexCache 加速長上下文推理 1.82 倍", comparison table
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -177,6 +179,88 @@ idxc_status sparse_mla_attn(const idxc_mla_desc *desc, const void *q, const void
  */
 idxc_status idx_overlap(const int32_t *t_a, const int32_t *t_b, int R, int topk, int32_t *counts,
                         void *stream);
+
+/*
+ * Serving-shaped batches over paged caches ([PPM] §§ "Real-world versnellingen
+ * op productiemodellen" (decode throughput of a saturated server) and
+ * "IndexCache in productie brengen" (vLLM and SGLang patches); [SAI]
+ * comparison table: paged memory allocation).
+ *
+ * A batch packs the query rows of num_seqs sequences one after another:
+ * sequence b owns rows query_start[b] .. query_start[b+1]-1, which are its
+ * last q_len_b = query_start[b+1] - query_start[b] positions, so row
+ * query_start[b] + i sits at position seq_lens[b] - q_len_b + i.  Decode
+ * tokens (q_len 1) and prefill chunks (q_len > 1) may be mixed freely.
+ * Caches are pools of num_blocks pages of block_size rows; sequence b's
+ * position s lives in page block_table[b][s / block_size], row
+ * s % block_size.  The same table serves the indexer key cache and the
+ * latent KV cache.
+ *
+ * query_start [num_seqs + 1], seq_lens [num_seqs] and block_table
+ * [num_seqs, max_blocks] are DEVICE int32 arrays.  Their contents must satisfy
+ * query_start[0] = 0, query_start nondecreasing with query_start[num_seqs] =
+ * total_q, q_len_b <= seq_lens[b] <= max_seq_len, and every page of a
+ * sequence's positions in [0, num_blocks).  The host cannot check them;
+ * values outside this contract give unspecified results but no out-of-bounds
+ * access (positions and pages are clamped).
+ */
+typedef struct {
+    int num_seqs, total_q, max_seq_len;
+    int num_blocks, block_size, max_blocks; /* block_size: power of two >= 64 */
+    int H, D, topk;
+    idxc_dtype q_dtype, k_dtype, w_dtype;
+} idxc_paged_indexer_desc;
+
+/* Workspace bytes of idx_score_topk_paged (scores of every row up to
+ * max_seq_len, plus row metadata). */
+idxc_status idx_score_topk_paged_workspace(const idxc_paged_indexer_desc *desc, size_t *bytes);
+
+/*
+ * idx_score_topk over a serving batch:
+ *   q       [total_q, H, D]          packed query rows (q_dtype)
+ *   k_cache [num_blocks, block_size, D] key pages (k_dtype)
+ *   w       [total_q, H]             head weights (w_dtype)
+ *   t_out   int32 [total_q, topk]    logical positions, as idx_score_topk
+ * Every row is scored against its sequence's keys 0..position (split over
+ * many workgroups, pages looked up per 64-key block) and its index set is
+ * the row top-k of those scores.  Supported as the split-key decode path of
+ * idx_score_topk: H = 64 with (FP8_E4M3, FP8_E4M3, BF16) D = 128 or
+ * (BF16, BF16, FP32) D in {32, 64, 128}.
+ */
+idxc_status idx_score_topk_paged(const idxc_paged_indexer_desc *desc, const void *q, const void *k_cache,
+                                 const int32_t *block_table, const int32_t *query_start, const int32_t *seq_lens,
+                                 const void *w, int32_t *t_out, void *ws, size_t ws_bytes, void *stream);
+
+/* The IndexCache router over a serving batch: as idx_cache_route with the
+ * Full-layer step replaced by idx_score_topk_paged; t_cache [total_q, topk]. */
+idxc_status idx_cache_route_paged(const char *pattern, int layer, const idxc_paged_indexer_desc *desc,
+                                  const void *q, const void *k_cache, const int32_t *block_table,
+                                  const int32_t *query_start, const int32_t *seq_lens, const void *w,
+                                  int32_t *t_cache, void *ws, size_t ws_bytes, void *stream, int *computed);
+
+typedef struct {
+    int num_seqs, total_q;
+    int num_blocks, block_size, max_blocks; /* block_size: power of two >= 1 */
+    int Hq, Dqk, Dv, topk;
+} idxc_paged_mla_desc;
+
+idxc_status sparse_mla_attn_paged_workspace(const idxc_paged_mla_desc *desc, size_t *bytes);
+
+/*
+ * sparse_mla_attn over a serving batch:
+ *   q        bf16 [total_q, Hq, Dqk]
+ *   kv_cache bf16 [num_blocks, block_size, Dqk] latent pages
+ *   t        int32 [total_q, topk] logical positions of the row's sequence
+ *            (entries < 0 or >= seq_len are skipped)
+ *   out      bf16 [total_q, Hq, Dv], lse optional fp32 [total_q, Hq]
+ * The index sets are turned into page-pool rows, then the contiguous kernel
+ * runs with the pool as one cache.  Same head/dimension support as
+ * sparse_mla_attn.
+ */
+idxc_status sparse_mla_attn_paged(const idxc_paged_mla_desc *desc, const void *q, const void *kv_cache,
+                                  const int32_t *block_table, const int32_t *query_start, const int32_t *seq_lens,
+                                  const int32_t *t, float sm_scale, void *out, float *lse, void *ws,
+                                  size_t ws_bytes, void *stream);
 
 /* Static text for a status code. */
 const char *idxc_status_str(idxc_status s);

@@ -16,6 +16,11 @@ Sources (page title and section):
         "Aandacht cachen met IndexCache"
   [AIB] aiboss88.com, "IndexCache - 清華大学とZhipuが共同開発した、
         スパースアテンション高速化技術。 - AiBoss", section "IndexCacheの技術的原理"
+  [SRV] serving batches over paged caches: parapluman.nl, sections
+        "Real-world versnellingen op productiemodellen" and "IndexCache in
+        productie brengen" (serving engines vLLM, SGLang); setupai.cc,
+        "IndexCache 加速長上下文推理 1.82 倍", comparison table (paged memory
+        allocation)
 
 Parity status of each function (pins live in tests/test_oracle_*.py):
   indexer_scores   pinned (hand-worked 8-token example, closed forms, H=1 case vs numpy)
@@ -23,6 +28,11 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
   route            pinned (hand-worked example, invariants)
   sparse_mla       pinned (dense attention via torch SDPA on CPU, closed forms)
   overlap          pinned (hand-worked rows, identical / disjoint / nested sets, symmetry)
+  gather_pages     pinned (hand-worked table, identity table = contiguous rows)
+  paged_indexer_topk, paged_sparse_mla
+                   pinned (one sequence over an identity table = the contiguous
+                   oracle; page permutations change nothing; a batch = its
+                   sequences taken one at a time)
   stack            parity unpinned: the way layers compose (residual add of the
                    head-summed attention output, then the seeded FFN stand-in)
                    is a reading, not something the pages fix.
@@ -299,3 +309,62 @@ def stack(pattern: str, x0_bits: np.ndarray, layers, topk_k: int, sm_scale: floa
         y = x1 @ bf16_bits_to_f64(lay["W"])
         x = bf16_bits_to_f64(f64_to_bf16_bits(x1 + y if residual_ffn else y))
     return f64_to_bf16_bits(x), ts
+
+
+# ---------------------------------------------------------------- serving batches over paged caches
+
+def gather_pages(cache: np.ndarray, table_row, n: int) -> np.ndarray:
+    """Rows 0..n-1 of one sequence from a page pool [num_blocks, bs, ...]: row s
+    is cache[table_row[s // bs], s % bs] [SRV].  The block-table addressing,
+    written out."""
+    bs = cache.shape[1]
+    s = np.arange(n)
+    return cache[np.asarray(table_row, dtype=np.int64)[s // bs], s % bs]
+
+
+def _batch_rows(query_start, rows):
+    """Per sequence: (b, first row, local rows to compute as flat indices)."""
+    qs = np.asarray(query_start, dtype=np.int64)
+    want = None if rows is None else set(int(r) for r in rows)
+    for b in range(qs.size - 1):
+        r0, r1 = int(qs[b]), int(qs[b + 1])
+        local = [r - r0 for r in range(r0, r1) if want is None or r in want]
+        if local:
+            yield b, r0, r1, np.asarray(local, dtype=np.int64)
+
+
+def paged_indexer_topk(q, k_cache, w, block_table, query_start, seq_lens, dtypes, topk_k: int, rows=None,
+                       nthreads=None):
+    """Index sets of a serving batch [SRV]: sequence b owns rows query_start[b] ..
+    query_start[b+1]-1, its last q_len positions; its keys are gathered from the
+    pages and the contiguous problem (one sequence, Lq = q_len, Lk = seq_len)
+    goes to indexer_topk.  q [total_q,H,D], k_cache [num_blocks,bs,D],
+    w [total_q,H] raw arrays.  Returns {row: T row} for the requested rows
+    (default all)."""
+    out = {}
+    for b, r0, r1, local in _batch_rows(query_start, rows):
+        L = int(seq_lens[b])
+        kb = gather_pages(k_cache, block_table[b], L)[None]
+        T, _ = indexer_topk(q[None, r0:r1], kb, w[None, r0:r1], dtypes, topk_k, rows=local, nthreads=nthreads)
+        for i, r in enumerate(local):
+            out[r0 + int(r)] = T[i]
+    return out
+
+
+def paged_sparse_mla(q, kv_cache, block_table, query_start, seq_lens, t, sm_scale: float, Dv: int, rows=None,
+                     nthreads=None):
+    """Sparse MLA of a serving batch [SRV]: row r of sequence b attends to the
+    latent rows t[r] of b (entries outside [0, seq_len_b) skipped), gathered
+    from the pages; the contiguous sparse_mla_dv does the arithmetic.
+    Returns {row: (out bf16 bits [Hq, Dv], lse [Hq])}."""
+    out = {}
+    t = np.asarray(t, dtype=np.int32)
+    for b, r0, r1, local in _batch_rows(query_start, rows):
+        L = int(seq_lens[b])
+        kvb = gather_pages(kv_cache, block_table[b], L)[None]
+        tb = t[r0:r1].copy()
+        tb[(tb < 0) | (tb >= L)] = -1
+        o, lse = sparse_mla_dv(q[None, r0:r1], kvb, tb[None], sm_scale, Dv, rows=local, nthreads=nthreads)
+        for i, r in enumerate(local):
+            out[r0 + int(r)] = (o[i], lse[i])
+    return out

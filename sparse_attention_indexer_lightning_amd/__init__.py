@@ -18,7 +18,9 @@ from . import _build
 __all__ = [
     "IdxcError", "lib", "idx_score_topk", "idx_score_topk_workspace", "idx_topk", "idx_topk_workspace",
     "idx_cache_route", "sparse_mla_attn", "sparse_mla_attn_workspace", "indexer_desc", "mla_desc",
-    "STATUS", "DTYPE",
+    "STATUS", "DTYPE", "idx_overlap", "overlap_matrix",
+    "idx_score_topk_paged", "idx_score_topk_paged_workspace", "idx_cache_route_paged",
+    "sparse_mla_attn_paged", "sparse_mla_attn_paged_workspace", "paged_indexer_desc", "paged_mla_desc",
 ]
 
 STATUS = {0: "IDXC_OK", -1: "IDXC_ERR_NULL", -2: "IDXC_ERR_SHAPE", -3: "IDXC_ERR_DTYPE",
@@ -40,6 +42,16 @@ class _IndexerDesc(ctypes.Structure):
 
 class _MlaDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("B", "Lq", "Lk", "Hq", "Dqk", "Dv", "topk")]
+
+
+class _PagedIndexerDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("num_seqs", "total_q", "max_seq_len", "num_blocks", "block_size",
+                                            "max_blocks", "H", "D", "topk", "q_dtype", "k_dtype", "w_dtype")]
+
+
+class _PagedMlaDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("num_seqs", "total_q", "num_blocks", "block_size", "max_blocks",
+                                            "Hq", "Dqk", "Dv", "topk")]
 
 
 _lib = None
@@ -79,6 +91,18 @@ def lib():
         L.sparse_mla_attn.argtypes = [mp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
         L.idx_overlap.restype = i32
         L.idx_overlap.argtypes = [vp, vp, i32, i32, vp, vp]
+        pdp = ctypes.POINTER(_PagedIndexerDesc)
+        pmp = ctypes.POINTER(_PagedMlaDesc)
+        L.idx_score_topk_paged_workspace.restype = i32
+        L.idx_score_topk_paged_workspace.argtypes = [pdp, szp]
+        L.idx_score_topk_paged.restype = i32
+        L.idx_score_topk_paged.argtypes = [pdp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.idx_cache_route_paged.restype = i32
+        L.idx_cache_route_paged.argtypes = [ctypes.c_char_p, i32, pdp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ip]
+        L.sparse_mla_attn_paged_workspace.restype = i32
+        L.sparse_mla_attn_paged_workspace.argtypes = [pmp, szp]
+        L.sparse_mla_attn_paged.restype = i32
+        L.sparse_mla_attn_paged.argtypes = [pmp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -237,4 +261,99 @@ def sparse_mla_attn(q, kv, t, sm_scale: float, Dv: int, out=None, lse=None, ws=N
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sparse_mla_attn(ctypes.byref(d), _p(q), _p(kv), _p(t), float(sm_scale), _p(out), _p(lse),
                                  _p(ws), wsb, _stream(stream, q.device)), "sparse_mla_attn")
+    return out, lse
+
+
+# ------------------------------------------------------------------ serving batches over paged caches
+#
+# q and w pack the query rows of all sequences ([total_q, H, D], [total_q, H]);
+# k_cache / kv_cache are page pools [num_blocks, block_size, row];
+# block_table int32 [num_seqs, max_blocks], query_start int32 [num_seqs + 1],
+# seq_lens int32 [num_seqs] are device tensors (see include/idxcache.h).
+
+
+def paged_indexer_desc(q, k_cache, w, block_table, query_start, topk: int, max_seq_len: int) -> _PagedIndexerDesc:
+    total_q, H, D = q.shape
+    num_blocks, block_size = k_cache.shape[:2]
+    return _PagedIndexerDesc(query_start.numel() - 1, total_q, max_seq_len, num_blocks, block_size,
+                             block_table.shape[1], H, D, topk, DTYPE.get(q.dtype, 0), DTYPE.get(k_cache.dtype, 0),
+                             DTYPE.get(w.dtype, 0))
+
+
+def paged_mla_desc(q, kv_cache, block_table, query_start, t, Dv: int) -> _PagedMlaDesc:
+    total_q, Hq, Dqk = q.shape
+    num_blocks, block_size = kv_cache.shape[:2]
+    return _PagedMlaDesc(query_start.numel() - 1, total_q, num_blocks, block_size, block_table.shape[1], Hq, Dqk,
+                         Dv, t.shape[-1])
+
+
+def idx_score_topk_paged_workspace(q, k_cache, w, block_table, query_start, topk: int, max_seq_len: int) -> int:
+    d = paged_indexer_desc(q, k_cache, w, block_table, query_start, topk, max_seq_len)
+    n = ctypes.c_size_t(0)
+    _check(lib().idx_score_topk_paged_workspace(ctypes.byref(d), ctypes.byref(n)), "idx_score_topk_paged_workspace")
+    return n.value
+
+
+def idx_score_topk_paged(q, k_cache, block_table, query_start, seq_lens, w, topk: int, max_seq_len: int,
+                         t_out=None, ws=None, stream=None):
+    """Indexer score + top-k of every row of a serving batch; returns T int32 [total_q, topk]
+    (logical positions of the row's sequence)."""
+    for name, x in (("q", q), ("k_cache", k_cache), ("w", w), ("block_table", block_table),
+                    ("query_start", query_start), ("seq_lens", seq_lens)):
+        _cuda_tensor(x, name)
+    if t_out is None:
+        t_out = torch.empty(q.shape[0], topk, dtype=torch.int32, device=q.device)
+    d = paged_indexer_desc(q, k_cache, w, block_table, query_start, topk, max_seq_len)
+    ws = _workspace(idx_score_topk_paged_workspace(q, k_cache, w, block_table, query_start, topk, max_seq_len),
+                    q.device, ws)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().idx_score_topk_paged(ctypes.byref(d), _p(q), _p(k_cache), _p(block_table), _p(query_start),
+                                      _p(seq_lens), _p(w), _p(t_out), _p(ws), wsb, _stream(stream, q.device)),
+           "idx_score_topk_paged")
+    return t_out
+
+
+def idx_cache_route_paged(pattern: str, layer: int, q, k_cache, block_table, query_start, seq_lens, w, t_cache,
+                          max_seq_len: int, ws=None, stream=None) -> bool:
+    """IndexCache router over a serving batch (t_cache int32 [total_q, topk]); True on Full layers."""
+    computed = ctypes.c_int(-1)
+    topk = t_cache.shape[-1]
+    if q is None:
+        d_ptr, wsb, dev = None, 0, t_cache.device
+    else:
+        d = paged_indexer_desc(q, k_cache, w, block_table, query_start, topk, max_seq_len)
+        d_ptr = ctypes.byref(d)
+        n = ctypes.c_size_t(0)
+        st = lib().idx_score_topk_paged_workspace(d_ptr, ctypes.byref(n))
+        ws = _workspace(n.value if st == 0 else 0, q.device, ws)
+        wsb = 0 if ws is None else ws.numel() * ws.element_size()
+        dev = q.device
+    _check(lib().idx_cache_route_paged(pattern.encode(), layer, d_ptr, _p(q), _p(k_cache), _p(block_table),
+                                       _p(query_start), _p(seq_lens), _p(w), _p(t_cache), _p(ws), wsb,
+                                       _stream(stream, dev), ctypes.byref(computed)), "idx_cache_route_paged")
+    return computed.value == 1
+
+
+def sparse_mla_attn_paged_workspace(q, kv_cache, block_table, query_start, t, Dv: int) -> int:
+    d = paged_mla_desc(q, kv_cache, block_table, query_start, t, Dv)
+    n = ctypes.c_size_t(0)
+    _check(lib().sparse_mla_attn_paged_workspace(ctypes.byref(d), ctypes.byref(n)), "sparse_mla_attn_paged_workspace")
+    return n.value
+
+
+def sparse_mla_attn_paged(q, kv_cache, block_table, query_start, seq_lens, t, sm_scale: float, Dv: int, out=None,
+                          lse=None, ws=None, stream=None):
+    """Sparse MLA attention over a serving batch; returns (out bf16 [total_q, Hq, Dv], lse or None)."""
+    for name, x in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table), ("query_start", query_start),
+                    ("seq_lens", seq_lens), ("t", t)):
+        _cuda_tensor(x, name)
+    total_q, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty(total_q, Hq, Dv, dtype=torch.bfloat16, device=q.device)
+    d = paged_mla_desc(q, kv_cache, block_table, query_start, t, Dv)
+    ws = _workspace(sparse_mla_attn_paged_workspace(q, kv_cache, block_table, query_start, t, Dv), q.device, ws)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sparse_mla_attn_paged(ctypes.byref(d), _p(q), _p(kv_cache), _p(block_table), _p(query_start),
+                                       _p(seq_lens), _p(t), float(sm_scale), _p(out), _p(lse), _p(ws), wsb,
+                                       _stream(stream, q.device)), "sparse_mla_attn_paged")
     return out, lse

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libidxcache.so")
-SOURCES = ["abi.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "sparse_mla_wide.hip", "overlap.hip"]
+SOURCES = ["abi.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip", "sparse_mla_wide.hip", "overlap.hip", "paged.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -127,6 +127,194 @@ idxc_status run_indexer(const idxc_indexer_desc *d, const void *q, const void *k
     return from_hip(e);
 }
 
+// Pattern validation shared by both routers; returns IDXC_OK and sets *full.
+idxc_status check_route(const char *pattern, int layer, bool *full) {
+    if (!pattern) return IDXC_ERR_NULL;
+    const size_t n = strlen(pattern);
+    if (n == 0 || pattern[0] != 'F') return IDXC_ERR_PATTERN;
+    for (size_t i = 0; i < n; ++i)
+        if (pattern[i] != 'F' && pattern[i] != 'S') return IDXC_ERR_PATTERN;
+    if (layer < 0 || (size_t)layer >= n) return IDXC_ERR_PATTERN;
+    *full = pattern[layer] == 'F';
+    return IDXC_OK;
+}
+
+// sparse_mla_attn after the null check; the paged entry point calls it with
+// the page pool as one cache (Lk = num_blocks * block_size).
+// validate_only: return after the checks, before any launch.
+idxc_status run_mla(const idxc_mla_desc *desc, const void *q, const void *kv, const int32_t *t, float sm_scale,
+                    void *out, float *lse, void *ws, size_t ws_bytes, void *stream, bool validate_only = false) {
+    const idxc_mla_desc &d = *desc;
+    if (d.B < 1 || d.Lq < 1 || d.Lk < 1 || d.Hq < 1 || d.Dqk < 1 || d.Dv < 1 || d.topk < 1 || d.Dv > d.Dqk)
+        return IDXC_ERR_SHAPE;
+    if ((size_t)d.B * d.Lq > (size_t)INT32_MAX / 2) return IDXC_ERR_SHAPE;
+    const bool small = d.Dqk == 32 && d.Dv == 32;
+    const bool mla = d.Dqk == 576 && d.Dv == 512;
+    if (!small && !mla) return IDXC_ERR_UNSUPPORTED;
+    if (small && (d.Hq % 4 != 0 || d.Hq > 128)) return IDXC_ERR_UNSUPPORTED;
+    if (mla && d.Hq % 16 != 0) return IDXC_ERR_UNSUPPORTED;
+    if (d.topk > kMaxTopk) return IDXC_ERR_UNSUPPORTED;
+    if (!(sm_scale > 0.f) || sm_scale > 1e30f) return IDXC_ERR_SHAPE;
+    if (!q || !kv || !t || !out) return IDXC_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(t, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)))
+        return IDXC_ERR_ALIGN;
+    const idxc::MlaWidePlan plan = idxc::mla_wide_plan(d.B, d.Lq, d.Hq, d.Dqk, d.Dv, d.topk);
+    if (plan.ok) {
+        if (plan.ws_bytes > 0 && !validate_only) {
+            if (!ws || ws_bytes < plan.ws_bytes) return IDXC_ERR_WORKSPACE;
+            if (!aligned(ws, 16)) return IDXC_ERR_ALIGN;
+        }
+        if (validate_only) return IDXC_OK;
+        idxc::MlaWideArgs w;
+        w.q = q; w.kv = kv; w.t = t; w.out = out; w.lse = lse; w.sm_scale = sm_scale;
+        w.B = d.B; w.Lq = d.Lq; w.Lk = d.Lk; w.Hq = d.Hq; w.topk = d.topk;
+        w.nchunk = plan.nchunk; w.chunk_rows = plan.chunk_rows;
+        w.part_o = ws;
+        w.part_lse = plan.ws_bytes > 0
+                         ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) +
+                                                     (size_t)d.B * d.Lq * d.Hq * plan.nchunk * d.Dv * 2)
+                         : nullptr;
+        return from_hip(idxc::launch_sparse_mla_wide(w, static_cast<hipStream_t>(stream)));
+    }
+    if (validate_only) return IDXC_OK;
+    idxc::MlaArgs a;
+    a.q = q; a.kv = kv; a.t = t; a.out = out; a.lse = lse; a.sm_scale = sm_scale;
+    a.B = d.B; a.Lq = d.Lq; a.Lk = d.Lk; a.Hq = d.Hq; a.Dqk = d.Dqk; a.Dv = d.Dv; a.topk = d.topk;
+    return from_hip(idxc::launch_sparse_mla(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- paged
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+int log2i(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Paged indexer workspace: row (sequence, position) pairs, row positions,
+// score rows of max_seq_len, then the row top-k's workspace.
+struct PagedIdxWs {
+    size_t info, pos, scores, topk, total;
+};
+PagedIdxWs paged_idx_ws(const idxc_paged_indexer_desc *d) {
+    PagedIdxWs w;
+    w.info = 0;
+    w.pos = align256((size_t)d->total_q * 8);
+    w.scores = w.pos + align256((size_t)d->total_q * 4);
+    w.topk = w.scores + align256((size_t)d->total_q * d->max_seq_len * sizeof(float));
+    w.total = w.topk + idxc::row_topk_ws_bytes(d->total_q, d->max_seq_len);
+    return w;
+}
+
+// The dense descriptor that the split-key scoring path sees for a serving
+// batch: total_q rows of one "sequence" whose score rows are max_seq_len long.
+idxc_indexer_desc paged_as_dense(const idxc_paged_indexer_desc *d) {
+    idxc_indexer_desc e;
+    e.B = 1;
+    e.Lq = d->total_q;
+    e.Lk = d->max_seq_len;
+    e.H = d->H;
+    e.D = d->D;
+    e.topk = d->topk;
+    e.q_dtype = d->q_dtype;
+    e.k_dtype = d->k_dtype;
+    e.w_dtype = d->w_dtype;
+    return e;
+}
+
+idxc_status check_paged_indexer_desc(const idxc_paged_indexer_desc *d) {
+    if (!d) return IDXC_ERR_NULL;
+    if (d->num_seqs < 1 || d->total_q < 1 || d->max_seq_len < 1 || d->num_blocks < 1 || d->max_blocks < 1 ||
+        d->H < 1 || d->D < 1 || d->topk < 1)
+        return IDXC_ERR_SHAPE;
+    if (!pow2(d->block_size) || d->block_size < 64) return IDXC_ERR_SHAPE;
+    if (d->max_seq_len > kMaxLen || (long long)d->max_blocks * d->block_size < d->max_seq_len) return IDXC_ERR_SHAPE;
+    if ((long long)d->num_blocks * d->block_size > (long long)INT32_MAX) return IDXC_ERR_SHAPE;
+    if ((long long)d->total_q * d->max_seq_len > ((long long)1 << 40)) return IDXC_ERR_SHAPE;
+    const idxc_indexer_desc e = paged_as_dense(d);
+    idxc_status st = check_indexer_desc(&e);
+    if (st != IDXC_OK && st != IDXC_ERR_SHAPE) return st;   // encodings, heads, topk
+    const idxc::IndexerArgs a = make_args(&e, nullptr, nullptr, nullptr, nullptr, nullptr);
+    if (!idxc::decode_supported(a)) return IDXC_ERR_UNSUPPORTED;
+    return IDXC_OK;
+}
+
+idxc_status run_indexer_paged(const idxc_paged_indexer_desc *d, const void *q, const void *k_cache,
+                              const int32_t *block_table, const int32_t *query_start, const int32_t *seq_lens,
+                              const void *w, int32_t *t, void *ws, hipStream_t stream) {
+    const PagedIdxWs lay = paged_idx_ws(d);
+    unsigned char *wsb = static_cast<unsigned char *>(ws);
+    int32_t *info = reinterpret_cast<int32_t *>(wsb + lay.info);
+    int32_t *pos = reinterpret_cast<int32_t *>(wsb + lay.pos);
+    float *scores = reinterpret_cast<float *>(wsb + lay.scores);
+    hipError_t e = idxc::launch_row_info(query_start, seq_lens, d->num_seqs, d->total_q, d->max_seq_len - 1, info,
+                                         pos, stream);
+    if (e != hipSuccess) return IDXC_ERR_HIP;
+    const idxc_indexer_desc dd = paged_as_dense(d);
+    idxc::IndexerArgs a = make_args(&dd, q, k_cache, w, t, scores);
+    idxc::PagedKeys pk;
+    pk.block_table = block_table;
+    pk.row_info = info;
+    pk.bs_log2 = log2i(d->block_size);
+    pk.max_blocks = d->max_blocks;
+    pk.num_blocks = d->num_blocks;
+    e = idxc::launch_indexer_scores(a, stream, &pk);
+    if (e != hipSuccess) return IDXC_ERR_HIP;
+    idxc::TopkArgs ta;
+    ta.scores = scores;
+    ta.row_pos = pos;
+    ta.R = d->total_q;
+    ta.Lk = d->max_seq_len;
+    ta.topk = d->topk;
+    ta.pos_Lq = 0;
+    ta.t_out = t;
+    ta.ws = wsb + lay.topk;
+    ta.ws_bytes = lay.total - lay.topk;
+    return from_hip(idxc::launch_row_topk(ta, stream));
+}
+
+idxc_status check_paged_indexer_call(const idxc_paged_indexer_desc *d, const void *q, const void *k_cache,
+                                     const int32_t *block_table, const int32_t *query_start,
+                                     const int32_t *seq_lens, const void *w, const int32_t *t, const void *ws,
+                                     size_t ws_bytes) {
+    idxc_status st = check_paged_indexer_desc(d);
+    if (st != IDXC_OK) return st;
+    if (!q || !k_cache || !block_table || !query_start || !seq_lens || !w || !t) return IDXC_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(t, 16) || !aligned(w, 4) || !aligned(block_table, 4) ||
+        !aligned(query_start, 4) || !aligned(seq_lens, 4))
+        return IDXC_ERR_ALIGN;
+    if (!ws || ws_bytes < paged_idx_ws(d).total) return IDXC_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return IDXC_ERR_ALIGN;
+    return IDXC_OK;
+}
+
+// Paged sparse MLA workspace: row metadata, pool-row index sets, then the
+// workspace of the contiguous kernel for total_q rows.
+struct PagedMlaWs {
+    size_t info, tphys, mla, total;
+};
+idxc_mla_desc paged_mla_as_dense(const idxc_paged_mla_desc *d) {
+    idxc_mla_desc m;
+    m.B = 1;
+    m.Lq = d->total_q;
+    m.Lk = (int)((long long)d->num_blocks * d->block_size);
+    m.Hq = d->Hq;
+    m.Dqk = d->Dqk;
+    m.Dv = d->Dv;
+    m.topk = d->topk;
+    return m;
+}
+PagedMlaWs paged_mla_ws(const idxc_paged_mla_desc *d, size_t mla_bytes) {
+    PagedMlaWs w;
+    w.info = 0;
+    w.tphys = align256((size_t)d->total_q * 8);
+    w.mla = w.tphys + align256((size_t)d->total_q * d->topk * 4);
+    w.total = w.mla + mla_bytes;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,12 +392,10 @@ idxc_status idx_cache_route(const char *pattern, int layer, const idxc_indexer_d
                             const void *k, const void *w, int32_t *t_cache, void *ws, size_t ws_bytes,
                             void *stream, int *computed) {
     if (!pattern || !t_cache) return IDXC_ERR_NULL;
-    const size_t n = strlen(pattern);
-    if (n == 0 || pattern[0] != 'F') return IDXC_ERR_PATTERN;
-    for (size_t i = 0; i < n; ++i)
-        if (pattern[i] != 'F' && pattern[i] != 'S') return IDXC_ERR_PATTERN;
-    if (layer < 0 || (size_t)layer >= n) return IDXC_ERR_PATTERN;
-    if (pattern[layer] == 'S') {
+    bool full;
+    const idxc_status pst = check_route(pattern, layer, &full);
+    if (pst != IDXC_OK) return pst;
+    if (!full) {
         // T of this layer is the cache as the nearest preceding Full layer left it.
         if (computed) *computed = 0;
         return IDXC_OK;
@@ -247,41 +433,99 @@ idxc_status sparse_mla_attn_workspace(const idxc_mla_desc *desc, size_t *bytes) 
 idxc_status sparse_mla_attn(const idxc_mla_desc *desc, const void *q, const void *kv, const int32_t *t,
                             float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
     if (!desc) return IDXC_ERR_NULL;
-    const idxc_mla_desc &d = *desc;
-    if (d.B < 1 || d.Lq < 1 || d.Lk < 1 || d.Hq < 1 || d.Dqk < 1 || d.Dv < 1 || d.topk < 1 || d.Dv > d.Dqk)
-        return IDXC_ERR_SHAPE;
-    if (d.Lk > kMaxLen || (size_t)d.B * d.Lq > (size_t)INT32_MAX / 2) return IDXC_ERR_SHAPE;
-    const bool small = d.Dqk == 32 && d.Dv == 32;
-    const bool mla = d.Dqk == 576 && d.Dv == 512;
-    if (!small && !mla) return IDXC_ERR_UNSUPPORTED;
-    if (small && (d.Hq % 4 != 0 || d.Hq > 128)) return IDXC_ERR_UNSUPPORTED;
-    if (mla && d.Hq % 16 != 0) return IDXC_ERR_UNSUPPORTED;
-    if (d.topk > kMaxTopk) return IDXC_ERR_UNSUPPORTED;
-    if (!(sm_scale > 0.f) || sm_scale > 1e30f) return IDXC_ERR_SHAPE;
-    if (!q || !kv || !t || !out) return IDXC_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(t, 4) || !aligned(out, 4) || (lse && !aligned(lse, 4)))
-        return IDXC_ERR_ALIGN;
-    const idxc::MlaWidePlan plan = idxc::mla_wide_plan(d.B, d.Lq, d.Hq, d.Dqk, d.Dv, d.topk);
-    if (plan.ok) {
-        if (plan.ws_bytes > 0) {
-            if (!ws || ws_bytes < plan.ws_bytes) return IDXC_ERR_WORKSPACE;
-            if (!aligned(ws, 16)) return IDXC_ERR_ALIGN;
-        }
-        idxc::MlaWideArgs w;
-        w.q = q; w.kv = kv; w.t = t; w.out = out; w.lse = lse; w.sm_scale = sm_scale;
-        w.B = d.B; w.Lq = d.Lq; w.Lk = d.Lk; w.Hq = d.Hq; w.topk = d.topk;
-        w.nchunk = plan.nchunk; w.chunk_rows = plan.chunk_rows;
-        w.part_o = ws;
-        w.part_lse = plan.ws_bytes > 0
-                         ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) +
-                                                     (size_t)d.B * d.Lq * d.Hq * plan.nchunk * d.Dv * 2)
-                         : nullptr;
-        return from_hip(idxc::launch_sparse_mla_wide(w, static_cast<hipStream_t>(stream)));
+    if (desc->Lk > kMaxLen) return IDXC_ERR_SHAPE;
+    return run_mla(desc, q, kv, t, sm_scale, out, lse, ws, ws_bytes, stream);
+}
+idxc_status idx_score_topk_paged_workspace(const idxc_paged_indexer_desc *desc, size_t *bytes) {
+    if (!bytes) return IDXC_ERR_NULL;
+    const idxc_status st = check_paged_indexer_desc(desc);
+    if (st != IDXC_OK) return st;
+    *bytes = paged_idx_ws(desc).total;
+    return IDXC_OK;
+}
+
+idxc_status idx_score_topk_paged(const idxc_paged_indexer_desc *desc, const void *q, const void *k_cache,
+                                 const int32_t *block_table, const int32_t *query_start, const int32_t *seq_lens,
+                                 const void *w, int32_t *t_out, void *ws, size_t ws_bytes, void *stream) {
+    const idxc_status st = check_paged_indexer_call(desc, q, k_cache, block_table, query_start, seq_lens, w, t_out,
+                                                    ws, ws_bytes);
+    if (st != IDXC_OK) return st;
+    return run_indexer_paged(desc, q, k_cache, block_table, query_start, seq_lens, w, t_out, ws,
+                             static_cast<hipStream_t>(stream));
+}
+
+idxc_status idx_cache_route_paged(const char *pattern, int layer, const idxc_paged_indexer_desc *desc,
+                                  const void *q, const void *k_cache, const int32_t *block_table,
+                                  const int32_t *query_start, const int32_t *seq_lens, const void *w,
+                                  int32_t *t_cache, void *ws, size_t ws_bytes, void *stream, int *computed) {
+    if (!pattern || !t_cache) return IDXC_ERR_NULL;
+    bool full;
+    idxc_status st = check_route(pattern, layer, &full);
+    if (st != IDXC_OK) return st;
+    if (!full) {
+        if (computed) *computed = 0;
+        return IDXC_OK;
     }
-    idxc::MlaArgs a;
-    a.q = q; a.kv = kv; a.t = t; a.out = out; a.lse = lse; a.sm_scale = sm_scale;
-    a.B = d.B; a.Lq = d.Lq; a.Lk = d.Lk; a.Hq = d.Hq; a.Dqk = d.Dqk; a.Dv = d.Dv; a.topk = d.topk;
-    return from_hip(idxc::launch_sparse_mla(a, static_cast<hipStream_t>(stream)));
+    st = check_paged_indexer_call(desc, q, k_cache, block_table, query_start, seq_lens, w, t_cache, ws, ws_bytes);
+    if (st != IDXC_OK) return st;
+    st = run_indexer_paged(desc, q, k_cache, block_table, query_start, seq_lens, w, t_cache, ws,
+                           static_cast<hipStream_t>(stream));
+    if (st == IDXC_OK && computed) *computed = 1;
+    return st;
+}
+
+idxc_status sparse_mla_attn_paged_workspace(const idxc_paged_mla_desc *desc, size_t *bytes) {
+    if (!desc || !bytes) return IDXC_ERR_NULL;
+    if (desc->total_q < 1 || desc->topk < 1 || desc->num_blocks < 1 || desc->max_blocks < 1 ||
+        !pow2(desc->block_size))
+        return IDXC_ERR_SHAPE;
+    if ((long long)desc->num_blocks * desc->block_size > (long long)INT32_MAX) return IDXC_ERR_SHAPE;
+    const idxc_mla_desc m = paged_mla_as_dense(desc);
+    size_t mla = 0;
+    const idxc_status st = sparse_mla_attn_workspace(&m, &mla);
+    if (st != IDXC_OK) return st;
+    *bytes = paged_mla_ws(desc, mla).total;
+    return IDXC_OK;
+}
+
+idxc_status sparse_mla_attn_paged(const idxc_paged_mla_desc *desc, const void *q, const void *kv_cache,
+                                  const int32_t *block_table, const int32_t *query_start, const int32_t *seq_lens,
+                                  const int32_t *t, float sm_scale, void *out, float *lse, void *ws,
+                                  size_t ws_bytes, void *stream) {
+    if (!desc) return IDXC_ERR_NULL;
+    const idxc_paged_mla_desc &d = *desc;
+    if (d.num_seqs < 1 || d.total_q < 1 || d.topk < 1 || d.num_blocks < 1 || d.max_blocks < 1 ||
+        !pow2(d.block_size))
+        return IDXC_ERR_SHAPE;
+    if ((long long)d.num_blocks * d.block_size > (long long)INT32_MAX) return IDXC_ERR_SHAPE;
+    if (!block_table || !query_start || !seq_lens || !t) return IDXC_ERR_NULL;
+    if (!aligned(block_table, 4) || !aligned(query_start, 4) || !aligned(seq_lens, 4) || !aligned(t, 4))
+        return IDXC_ERR_ALIGN;
+    const idxc_mla_desc m = paged_mla_as_dense(desc);
+    size_t mla = 0;
+    idxc_status st = sparse_mla_attn_workspace(&m, &mla);
+    if (st != IDXC_OK) return st;
+    const PagedMlaWs lay = paged_mla_ws(desc, mla);
+    if (!ws || ws_bytes < lay.total) return IDXC_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return IDXC_ERR_ALIGN;
+    // the contiguous kernel's own checks run before anything is enqueued
+    unsigned char *wsb = static_cast<unsigned char *>(ws);
+    int32_t *info = reinterpret_cast<int32_t *>(wsb + lay.info);
+    int32_t *tphys = reinterpret_cast<int32_t *>(wsb + lay.tphys);
+    st = run_mla(&m, q, kv_cache, tphys, sm_scale, out, lse, wsb + lay.mla, lay.total - lay.mla, stream, true);
+    if (st != IDXC_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int bs_log2 = log2i(d.block_size);
+    hipError_t e = idxc::launch_row_info(query_start, seq_lens, d.num_seqs, d.total_q,
+                                         (int)(((long long)d.max_blocks << bs_log2) - 1 < INT32_MAX
+                                                   ? ((long long)d.max_blocks << bs_log2) - 1
+                                                   : INT32_MAX),
+                                         info, nullptr, hs);
+    if (e != hipSuccess) return IDXC_ERR_HIP;
+    e = idxc::launch_translate_index(t, info, seq_lens, block_table, d.total_q, d.topk, bs_log2, d.max_blocks,
+                                     d.num_blocks, tphys, hs);
+    if (e != hipSuccess) return IDXC_ERR_HIP;
+    return run_mla(&m, q, kv_cache, tphys, sm_scale, out, lse, wsb + lay.mla, lay.total - lay.mla, stream);
 }
 
 }  // extern "C"

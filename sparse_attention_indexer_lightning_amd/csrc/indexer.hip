@@ -901,6 +901,14 @@ struct ScoreParams {
     float *scores;
     int B, Lq, Lk, split;
     Enc w_enc;
+    // paged key cache (decode_scores_kernel<.., true>): k is the page pool
+    // [num_blocks][block_size][row], block_table [B][max_blocks] maps a
+    // sequence's key s to page block_table[b][s >> bs_log2], row s & (bs-1);
+    // row_info [rows] gives each query row's (sequence, position); scores rows
+    // are Lk apart (Lk = the longest sequence)
+    const int32_t *block_table;
+    const int2 *row_info;
+    int bs_log2, max_blocks, num_blocks;
 };
 
 constexpr int kDecodeWaves = 4;
@@ -908,14 +916,23 @@ constexpr int kComputeUnits = 256;   // MI355X
 
 // 64 heads of one query against a contiguous key range; B operands are read
 // straight from HBM (each key is used by exactly one query row here).
-template <Enc E, int D>
-__global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(ScoreParams p) {
+template <Enc E, int D, bool Paged>
+__global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_scores_kernel(ScoreParams p) {
     using S = Shape<E, D>;
     constexpr int H = 64;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4, n = lane & 15;
+    const int tid = threadIdx.x, lane = tid % kWave, g = lane >> 4, n = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int row = blockIdx.y;
-    const int b = row / p.Lq, i = row % p.Lq;
-    const int pos = p.Lk - p.Lq + i;
+    int b, pos;
+    if constexpr (Paged) {
+        const int2 ri = p.row_info[row];
+        b = __builtin_amdgcn_readfirstlane(ri.x);
+        pos = __builtin_amdgcn_readfirstlane(ri.y);
+    } else {
+        b = row / p.Lq;
+        pos = p.Lk - p.Lq + row % p.Lq;
+    }
     const int s0 = blockIdx.x * p.split;
     const int s1 = min(s0 + p.split, p.Lk);
     float *out = p.scores + (size_t)row * p.Lk;
@@ -936,6 +953,17 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
         }
     }
     const unsigned char *kb = p.k + (size_t)b * p.Lk * S::ROWB;
+    // paged: address of key s of this row's sequence (s <= pos); pages are
+    // clamped to the pool so that no table value can address outside it
+    // (the table is read through the constant address space: its loads are
+    // uniform and go through the scalar cache, off the vector-memory counter
+    // that the key loads are waited on)
+    const __attribute__((address_space(4))) int32_t *bt =
+        Paged ? (const __attribute__((address_space(4))) int32_t *)(p.block_table + (size_t)b * p.max_blocks) : nullptr;
+    auto page_base = [&](int s) -> const unsigned char * {
+        const int pg = min(max(bt[s >> p.bs_log2], 0), p.num_blocks - 1);
+        return p.k + (((size_t)pg << p.bs_log2) + (s & ((1 << p.bs_log2) - 1))) * S::ROWB;
+    };
     if constexpr (kMfma32) {
         // the keys of the next block are loaded while the current one is
         // scored (two register buffers used in turn, so that no loaded value
@@ -944,12 +972,28 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
         // key, so that every iteration issues the same loads and the
         // compiler's waits stay exact.
         constexpr int STRIDE = kDecodeWaves * KB;
-        auto load_block = [&](v8i (&B)[2][2], int base) {
+        // paged: a 64-key block lies in one page (pages hold a multiple of 64
+        // keys); past the last valid key the last valid block is read again.
+        // The page of a block is looked up (scalar load) one block before its
+        // keys are loaded.
+        auto block_page = [&](int base) -> const unsigned char * {
+            if constexpr (Paged) return page_base(min(base, pos) & ~(KB - 1));
+            else return nullptr;
+        };
+        auto load_block = [&](v8i (&B)[2][2], int base, const unsigned char *pb) {
+            if constexpr (Paged) {
 #pragma unroll
-            for (int cf = 0; cf < 2; ++cf) {
-                const int key = min(base + 32 * cf + (lane & 31), p.Lk - 1);
+                for (int cf = 0; cf < 2; ++cf)
 #pragma unroll
-                for (int st = 0; st < 2; ++st) B[cf][st] = load32(kb + (size_t)key * S::ROWB + 64 * st + 32 * (lane >> 5));
+                    for (int st = 0; st < 2; ++st)
+                        B[cf][st] = load32(pb + (size_t)(32 * cf + (lane & 31)) * S::ROWB + 64 * st + 32 * (lane >> 5));
+            } else {
+#pragma unroll
+                for (int cf = 0; cf < 2; ++cf) {
+                    const int key = min(base + 32 * cf + (lane & 31), p.Lk - 1);
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) B[cf][st] = load32(kb + (size_t)key * S::ROWB + 64 * st + 32 * (lane >> 5));
+                }
             }
         };
         auto score_block = [&](const v8i (&B)[2][2], int base) {
@@ -960,15 +1004,21 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
         const int last = min(s1, pos + 1);        // keys at or before the query position
         int base = s0 + wave * KB;
         v8i B0[2][2], B1[2][2];
-        if (base < last) load_block(B0, base);
+        const unsigned char *pg1 = nullptr;
+        if (base < last) {
+            load_block(B0, base, block_page(base));
+            pg1 = block_page(base + STRIDE);
+        }
         for (; base < last; base += 2 * STRIDE) {
-            load_block(B1, base + STRIDE);
+            load_block(B1, base + STRIDE, pg1);
+            const unsigned char *pg2 = block_page(base + 2 * STRIDE);
             score_block(B0, base);
             if (base + STRIDE >= last) {
                 base += STRIDE;
                 break;
             }
-            load_block(B0, base + 2 * STRIDE);
+            load_block(B0, base + 2 * STRIDE, pg2);
+            pg1 = block_page(base + 3 * STRIDE);
             score_block(B1, base + STRIDE);
         }
         for (; base < s1; base += STRIDE) {
@@ -987,8 +1037,13 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_scores_kernel(Sco
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = base + 16 * j + n;
-            if (key < p.Lk) load_frag<E, D>(Bf[j], kb + (size_t)key * S::ROWB, g);
-            else zero_frag<E, D>(Bf[j]);
+            if constexpr (Paged) {
+                if (key <= pos) load_frag<E, D>(Bf[j], page_base(key), g);
+                else zero_frag<E, D>(Bf[j]);
+            } else {
+                if (key < p.Lk) load_frag<E, D>(Bf[j], kb + (size_t)key * S::ROWB, g);
+                else zero_frag<E, D>(Bf[j]);
+            }
         }
         float part[4];
 #pragma unroll
@@ -1091,7 +1146,7 @@ hipError_t launch_prefill_d(const IndexerArgs &a, hipStream_t st) {
 }
 
 template <Enc E, int D>
-hipError_t launch_decode_d(const IndexerArgs &a, hipStream_t st) {
+hipError_t launch_decode_d(const IndexerArgs &a, hipStream_t st, const PagedKeys *pk = nullptr) {
     ScoreParams p;
     p.q = static_cast<const unsigned char *>(a.q);
     p.k = static_cast<const unsigned char *>(a.k);
@@ -1107,8 +1162,21 @@ hipError_t launch_decode_d(const IndexerArgs &a, hipStream_t st) {
     const int want = std::max(1, std::min(max_split, (2 * kComputeUnits + rows - 1) / rows));
     p.split = ((a.Lk + want - 1) / want + 255) / 256 * 256;
     const int nsplit = (a.Lk + p.split - 1) / p.split;
-    hipLaunchKernelGGL((decode_scores_kernel<E, D>), dim3((unsigned)nsplit, (unsigned)(a.B * a.Lq)),
-                       dim3(kDecodeWaves * kWave), 0, st, p);
+    if (pk) {
+        p.block_table = pk->block_table;
+        p.row_info = reinterpret_cast<const int2 *>(pk->row_info);
+        p.bs_log2 = pk->bs_log2;
+        p.max_blocks = pk->max_blocks;
+        p.num_blocks = pk->num_blocks;
+        hipLaunchKernelGGL((decode_scores_kernel<E, D, true>), dim3((unsigned)nsplit, (unsigned)(a.B * a.Lq)),
+                           dim3(kDecodeWaves * kWave), 0, st, p);
+    } else {
+        p.block_table = nullptr;
+        p.row_info = nullptr;
+        p.bs_log2 = p.max_blocks = p.num_blocks = 0;
+        hipLaunchKernelGGL((decode_scores_kernel<E, D, false>), dim3((unsigned)nsplit, (unsigned)(a.B * a.Lq)),
+                           dim3(kDecodeWaves * kWave), 0, st, p);
+    }
     return hipGetLastError();
 }
 
@@ -1133,13 +1201,13 @@ bool decode_supported(const IndexerArgs &a) {
     return a.D == 32 || a.D == 64 || a.D == 128;
 }
 
-hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t st) {
+hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t st, const PagedKeys *pk) {
     if (a.qk_enc == Enc::FP8) {
-        if (a.D == 128) return launch_decode_d<Enc::FP8, 128>(a, st);
+        if (a.D == 128) return launch_decode_d<Enc::FP8, 128>(a, st, pk);
     } else if (a.qk_enc == Enc::BF16) {
-        if (a.D == 32) return launch_decode_d<Enc::BF16, 32>(a, st);
-        if (a.D == 64) return launch_decode_d<Enc::BF16, 64>(a, st);
-        if (a.D == 128) return launch_decode_d<Enc::BF16, 128>(a, st);
+        if (a.D == 32) return launch_decode_d<Enc::BF16, 32>(a, st, pk);
+        if (a.D == 64) return launch_decode_d<Enc::BF16, 64>(a, st, pk);
+        if (a.D == 128) return launch_decode_d<Enc::BF16, 128>(a, st, pk);
     }
     return hipErrorInvalidValue;
 }

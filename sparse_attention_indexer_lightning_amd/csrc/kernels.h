@@ -22,10 +22,35 @@ struct IndexerArgs {
 bool prefill_fits(const IndexerArgs &a);
 hipError_t launch_indexer_prefill(const IndexerArgs &a, hipStream_t s);
 
+// Paged key cache for launch_indexer_scores: k is the page pool
+// [num_blocks][1 << bs_log2][row] (bs_log2 >= 6), block_table [B][max_blocks]
+// holds each sequence's pages in order, row_info [B*Lq] (int2) each query
+// row's (sequence, position).  a.B * a.Lq is then the number of query rows
+// and a.Lk the score row stride (>= every position + 1).
+struct PagedKeys {
+    const int32_t *block_table;
+    const int32_t *row_info;
+    int bs_log2, max_blocks, num_blocks;
+};
+
 // Scores of every (query, key <= position) into a.scores [B*Lq, Lk], keys
 // split over many workgroups; -inf beyond each query's position.
 bool decode_supported(const IndexerArgs &a);
-hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t s);
+hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t s, const PagedKeys *paged = nullptr);
+
+// Serving metadata: row_info[r] = (sequence, position) of query row r from
+// query_start [B+1] (rows of sequence b are query_start[b]..[b+1]-1, the last
+// ones of that sequence) and seq_lens [B]; row_pos [rows] (optional) gets the
+// positions alone.  Values are clamped so that every row maps to a valid
+// sequence and a position in [0, max_pos].
+hipError_t launch_row_info(const int32_t *query_start, const int32_t *seq_lens, int B, int rows, int max_pos,
+                           int32_t *row_info, int32_t *row_pos, hipStream_t s);
+// Logical -> pool row indices of a paged latent cache: out[r][j] =
+// page(t[r][j]) * bs + t[r][j] % bs for 0 <= t < seq_len of row r's
+// sequence, -1 otherwise.
+hipError_t launch_translate_index(const int32_t *t, const int32_t *row_info, const int32_t *seq_lens,
+                                  const int32_t *block_table, int rows, int topk, int bs_log2, int max_blocks,
+                                  int num_blocks, int32_t *out, hipStream_t s);
 
 // Exact per-row top-k of fp32 scores [R, Lk] (ties to the lower index,
 // ascending output, -1 padding).  row_pos may be NULL (all Lk keys valid).

@@ -185,3 +185,83 @@ def test_overlap_rejections():
     assert L.idx_overlap(None, FAKE, 4, 8, FAKE, None) == NULL
     assert L.idx_overlap(FAKE, FAKE, 4, 8, None, None) == NULL
     assert L.idx_overlap(ctypes.c_void_p(0x10002), FAKE, 4, 8, FAKE, None) == ALIGN
+
+
+# ---------------------------------------------------------------- serving batches over paged caches
+
+def pdesc(num_seqs=2, total_q=3, max_seq_len=1000, num_blocks=40, block_size=64, max_blocks=16, H=64, D=128,
+          topk=64, qd=FP8, kd=FP8, wd=BF16):
+    return sa._PagedIndexerDesc(num_seqs, total_q, max_seq_len, num_blocks, block_size, max_blocks, H, D, topk, qd,
+                                kd, wd)
+
+
+def pscore(d, ws=FAKE, wsb=1 << 40, **ptrs):
+    p = dict(q=FAKE, k=FAKE, bt=FAKE, qs=FAKE, sl=FAKE, w=FAKE, t=FAKE)
+    p.update(ptrs)
+    return sa.lib().idx_score_topk_paged(ctypes.byref(d) if d is not None else None, p["q"], p["k"], p["bt"],
+                                         p["qs"], p["sl"], p["w"], p["t"], ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_size=32), SHAPE), (dict(block_size=96), SHAPE), (dict(max_blocks=15), SHAPE),
+    (dict(num_seqs=0), SHAPE), (dict(total_q=0), SHAPE), (dict(num_blocks=0), SHAPE),
+    (dict(max_seq_len=0), SHAPE), (dict(H=32), UNSUP), (dict(topk=4096), UNSUP), (dict(qd=BF16), DTYPE),
+])
+def test_paged_indexer_descriptor_rejections(kw, code):
+    assert pscore(pdesc(**kw)) == code
+
+
+def test_paged_indexer_pointers_and_workspace():
+    d = pdesc()
+    n = ctypes.c_size_t(0)
+    assert sa.lib().idx_score_topk_paged_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
+    # row metadata, score rows of max_seq_len, the top-k's workspace
+    assert n.value >= 3 * 1000 * 4 + 3 * 12
+    assert pscore(None) == NULL
+    for key in ("q", "k", "bt", "qs", "sl", "w", "t"):
+        assert pscore(d, **{key: None}) == NULL, key
+    assert pscore(d, q=FAKE_ODD) == ALIGN
+    assert pscore(d, ws=None, wsb=0) == WS
+    assert pscore(d, wsb=n.value - 1) == WS
+    assert pscore(d, ws=ctypes.c_void_p(0x10010), wsb=n.value) == ALIGN
+
+
+def test_paged_router_pattern_rules_and_shared_layer():
+    L = sa.lib()
+    d = pdesc()
+    done = ctypes.c_int(-1)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert L.idx_cache_route_paged(b"SF", 0, ctypes.byref(d), *args, ctypes.byref(done)) == PATTERN
+    assert L.idx_cache_route_paged(b"FS", 2, ctypes.byref(d), *args, ctypes.byref(done)) == PATTERN
+    assert L.idx_cache_route_paged(b"FS", 1, None, None, None, None, None, None, None, FAKE, None, 0, None,
+                                   ctypes.byref(done)) == OK
+    assert done.value == 0
+    bad = pdesc(block_size=48)
+    assert L.idx_cache_route_paged(b"FS", 0, ctypes.byref(bad), *args, ctypes.byref(done)) == SHAPE
+
+
+def test_paged_mla_rejections():
+    L = sa.lib()
+
+    def pm(num_seqs=2, total_q=3, num_blocks=10, block_size=16, max_blocks=8, Hq=64, Dqk=576, Dv=512, topk=64,
+           ws=FAKE, wsb=1 << 40, **ptrs):
+        d = sa._PagedMlaDesc(num_seqs, total_q, num_blocks, block_size, max_blocks, Hq, Dqk, Dv, topk)
+        p = dict(q=FAKE, kv=FAKE, bt=FAKE, qs=FAKE, sl=FAKE, t=FAKE, out=FAKE)
+        p.update(ptrs)
+        return L.sparse_mla_attn_paged(ctypes.byref(d), p["q"], p["kv"], p["bt"], p["qs"], p["sl"], p["t"], 0.1,
+                                       p["out"], None, ws, wsb, None)
+
+    assert pm(block_size=24) == SHAPE
+    assert pm(total_q=0) == SHAPE
+    assert pm(num_blocks=1 << 20, block_size=1 << 12) == SHAPE   # pool rows beyond int32
+    assert pm(Hq=24) == UNSUP
+    assert pm(Dqk=128, Dv=128) == UNSUP
+    assert pm(bt=None) == NULL
+    assert pm(q=None) == NULL
+    assert pm(out=None) == NULL
+    assert pm(kv=FAKE_ODD) == ALIGN
+    assert pm(ws=None, wsb=0) == WS
+    n = ctypes.c_size_t(0)
+    d = sa._PagedMlaDesc(2, 3, 10, 16, 8, 64, 576, 512, 64)
+    assert L.sparse_mla_attn_paged_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
+    assert n.value >= 3 * 8 + 3 * 64 * 4
