@@ -120,6 +120,32 @@ def decode(args, torch, sa, inputs):
     t_idx = timed(lambda: sa.idx_cache_route("FSSS", 0, q, k, w, t, ws=ws))
     t_att = timed(lambda: sa.sparse_mla_attn(qa, kv, t, scale, wl.Dv, out=out))
     t_f = t_idx + t_att
+
+    # the same step as a serving batch: caches in pools of 64-row pages at
+    # random slots (one shared block table), query rows packed
+    bs = 64
+    npg = (wl.Lk + bs - 1) // bs
+    g = torch.Generator(device="cpu").manual_seed(11)
+    perm = torch.randperm(wl.B * npg, generator=g).to(dev)
+    table = perm.view(wl.B, npg).to(torch.int32)
+    k_pool = torch.empty(wl.B * npg, bs, wl.D, dtype=k.dtype, device=dev)
+    k_pool[perm.long()] = k.view(wl.B * npg, bs, wl.D)
+    kv_pool = torch.empty(wl.B * npg, bs, wl.Dqk, dtype=kv.dtype, device=dev)
+    kv_pool[perm.long()] = kv.view(wl.B * npg, bs, wl.Dqk)
+    qs = torch.arange(wl.B + 1, dtype=torch.int32, device=dev)
+    sl = torch.full((wl.B,), wl.Lk, dtype=torch.int32, device=dev)
+    qp, wp, qap = q.view(wl.B, wl.H, wl.D), w.view(wl.B, wl.H), qa.view(wl.B, wl.Hq, wl.Dqk)
+    tp = torch.empty(wl.B, wl.topk, dtype=torch.int32, device=dev)
+    outp = torch.empty(wl.B, wl.Hq, wl.Dv, dtype=torch.bfloat16, device=dev)
+    wsp = torch.empty(sa.idx_score_topk_paged_workspace(qp, k_pool, wp, table, qs, wl.topk, wl.Lk),
+                      dtype=torch.uint8, device=dev)
+    wsa = torch.empty(max(1, sa.sparse_mla_attn_paged_workspace(qap, kv_pool, table, qs, tp, wl.Dv)),
+                      dtype=torch.uint8, device=dev)
+    t_pidx = timed(lambda: sa.idx_score_topk_paged(qp, k_pool, table, qs, sl, wp, wl.topk, wl.Lk, t_out=tp, ws=wsp))
+    t_patt = timed(lambda: sa.sparse_mla_attn_paged(qap, kv_pool, table, qs, sl, tp, scale, wl.Dv, out=outp,
+                                                    ws=wsa))
+    same_t = bool(torch.equal(tp, t.view(wl.B, wl.topk)))
+    del k_pool, kv_pool
     gathered = wl.B * wl.Lq * wl.topk * wl.Dqk * 2
     key_bytes = wl.B * wl.Lk * wl.D
     tok = wl.B * wl.Lq
@@ -134,6 +160,12 @@ def decode(args, torch, sa, inputs):
         "gather_GBs": round(gathered / (t_att * 1e-3) / 1e9, 1),
         "gather_frac_hbm": round(gathered / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "note": "caches flushed before each timed call; one layer = one call each",
+        "serving_paged": {
+            "block_size": bs, "pages": "random slots of one pool, shared block table",
+            "indexer_topk_ms": round(t_pidx, 4), "sparse_mla_ms": round(t_patt, 4),
+            "full_layer_tok_s": round(tok / ((t_pidx + t_patt) * 1e-3), 1),
+            "t_identical_to_contiguous": same_t,
+        },
     }
 
 
