@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the retention-ratio sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     ap.add_argument("--profile-only", action="store_true", help="run warmup+steps of the headline only")
-    ap.add_argument("--profile", choices=["prefill", "decode", "copy"],
+    ap.add_argument("--profile", choices=["prefill", "decode", "mla_prefill", "copy"],
                     help="run warmup+steps of one workload (for profiler runs) and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write the headline kernel's HBM traffic from rocprofv3 counter runs in DIR "
@@ -242,6 +242,15 @@ def profile_run(args, torch, sa, inputs):
         ws = torch.empty(sa.idx_score_topk_workspace(q, k, w, wl.topk), dtype=torch.uint8, device=dev)
         for _ in range(args.warmup + args.steps):
             sa.idx_cache_route("F", 0, q, k, w, t, ws=ws)
+            sa.sparse_mla_attn(qa, kv, t, 1.0 / math.sqrt(wl.Dqk), wl.Dv, out=out)
+    elif args.profile == "mla_prefill":
+        wl = inputs.WORKLOADS["stack_32k"]
+        qa, kv = inputs.attention_inputs(wl, 0, dev)
+        q, k, w = inputs.indexer_inputs(wl, 0, dev)
+        t = sa.idx_score_topk(q, k, w, wl.topk)
+        del q, k, w
+        out = torch.empty(wl.B, wl.Lq, wl.Hq, wl.Dv, dtype=torch.bfloat16, device=dev)
+        for _ in range(args.warmup + args.steps):
             sa.sparse_mla_attn(qa, kv, t, 1.0 / math.sqrt(wl.Dqk), wl.Dv, out=out)
     else:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
