@@ -376,36 +376,37 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
                     for (int t = 0; t < 2; ++t) vbs[m2][t] = opaque(vb[m2][t]);
 #pragma unroll
                 for (int cp = 0; cp < 2; ++cp) pbs[cp] = opaque(pbase[cp]);
-                // software pipeline over the 16 (k-step, output block) stages:
-                // the V^T reads of stage i+2 and the P^T reads of the next
-                // k-step are in flight while stage i runs on the MFMA unit
-                auto read_v = [&](int i) -> v8bf {
-                    const int cp = i >> 3, mb = i & 7;
-                    const v4s lo = lds_read_tr16(prv + vbs[mb & 1][0] + OCT_BYTES * (mb >> 1) + 2048 * cp);
-                    const v4s hi = lds_read_tr16(prv + vbs[mb & 1][1] + OCT_BYTES * (mb >> 1) + 2048 * cp);
-                    return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                };
-                auto read_p = [&](int cp, int nb) -> v8bf {
-                    return __builtin_bit_cast(v8bf, lds_read_b128((lds_u8 *)sm.ptile[par] + pbs[cp] + 2048 * nb));
-                };
-                v8bf pb[2][2], va[3];
-                pb[0][0] = read_p(0, 0);
-                pb[0][1] = read_p(0, 1);
-                va[0] = read_v(0);
-                va[1] = read_v(1);
+                // two batches, one per k-step of 16 rows: all V^T and P^T
+                // operands of a batch are read at once.  The consumer has LDS
+                // copies in flight, so every wait for an LDS read is a full
+                // one; batching leaves one exposed wait per tile, and the
+                // second batch's reads complete under the first batch's MFMAs.
+                auto read_batch = [&](int cp, v8bf (&va)[8], v8bf (&pb)[2]) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i + 2 < 16) va[(i + 2) % 3] = read_v(i + 2);
-                    if (i == 4) {
-                        pb[1][0] = read_p(1, 0);
-                        pb[1][1] = read_p(1, 1);
+                    for (int nb = 0; nb < 2; ++nb)
+                        pb[nb] = __builtin_bit_cast(v8bf, lds_read_b128((lds_u8 *)sm.ptile[par] + pbs[cp] + 2048 * nb));
+#pragma unroll
+                    for (int mb = 0; mb < 8; ++mb) {
+                        const v4s lo = lds_read_tr16(prv + vbs[mb & 1][0] + OCT_BYTES * (mb >> 1) + 2048 * cp);
+                        const v4s hi = lds_read_tr16(prv + vbs[mb & 1][1] + OCT_BYTES * (mb >> 1) + 2048 * cp);
+                        va[mb] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                    const int cp = i >> 3, mb = i & 7;
+                };
+                v8bf va0[8], va1[8], pb0[2], pb1[2];
+                read_batch(0, va0, pb0);
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): batch 0 landed
+                __builtin_amdgcn_sched_barrier(0);
+                read_batch(1, va1, pb1);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma_bf16_32x32x16(va[i % 3], pb[cp][nb], o[mb][nb]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma_bf16_32x32x16(va0[mb], pb0[nb], o[mb][nb]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma_bf16_32x32x16(va1[mb], pb1[nb], o[mb][nb]);
             }
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OCTETS + 1));
             if (lane < 16) sm.ring[(s + 4) & (RING - 1)][16 * c + lane] = pend;
