@@ -71,6 +71,15 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf &a, const v8bf &b, 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// s_waitcnt immediate for vmcnt(n) with the other counters unconstrained
+// (vmcnt is split over bits 3:0 and 15:14).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Workgroup barrier ordering LDS accesses only.  __syncthreads also waits for
+// every global load in flight (vmcnt(0)); kernels that keep loads in flight
+// across the barrier wait for them with explicit vmcnt bounds instead.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m) { return __shfl_xor(v, m, kWave); }
 

@@ -217,6 +217,10 @@ __device__ __forceinline__ float score64_mfma32(const Q32 &Q, KB32 kb) {
     return score64_mfma32_b(Q, B);
 }
 
+// The value is computed before this point: a scheduling anchor that keeps an
+// epilogue in the phase whose MFMAs it is meant to overlap.
+__device__ __forceinline__ void keep_here(float &x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
@@ -543,7 +547,7 @@ __device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, u
 // and read again; exact selection is the last resort.
 // Precondition: st.cnt >= k.
 template <typename IdxT>
-__device__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
+__device__ __forceinline__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
                                uint32_t *pad_k, IdxT *pad_i, int lane) {
     if (!st.binned) rebuild_hist<IdxT>(bkey, st, buffer_min<IdxT>(bkey, st.cnt, lane), hist, lane);
     for (int attempt = 0;; ++attempt) {
@@ -639,6 +643,9 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int nblk = pmax / KB + 1;
 
     constexpr bool kMfma32 = E == Enc::FP8 && H == 64 && D == 128;
+    // the pipelined sweep below needs eight wavefronts, which the LDS plan
+    // always gives with 16-bit candidate indices (keys up to 65536)
+    constexpr bool kPipe = kMfma32 && sizeof(IdxT) == 2;
     Q32 Q32f;
     if constexpr (kMfma32) {
         const int i = i0 + wave;
@@ -707,6 +714,155 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             }
         }
     };
+    // Streaming selection of one 64-key block (lane l: key base + l, score sc)
+    // for the wave's row (one row per wavefront); returns whether the row's
+    // buffer must be compacted before the next block.
+    auto select_binned = [&](float sc, int base) -> bool {
+        const int i = i0 + wave;
+        const int pos = off + i;
+        if (i >= p.Lq || base > pos) return false;
+        const int s = base + lane;
+        if (p.scores && s < p.Lk) p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc : -INFINITY;
+        const bool cand = s <= pos && sc > st.thr_f;
+        const uint64_t m = ballot(cand);
+        if (m) {
+            uint32_t *bk = bkey_all + (size_t)wave * p.cap;
+            IdxT *bi = bidx_all + (size_t)wave * p.cap;
+            const int at = st.cnt + lanes_below(m);
+            const uint32_t key = score_key(sc);
+            if (cand) {
+                bk[at] = key;
+                bi[at] = (IdxT)s;
+            }
+            if (st.binned) atomicAdd(&hist[cand ? bin_of(key, st.lo) : 256u + lane], 1u);
+            st.cnt += __popcll(m);
+        }
+        return st.cnt > p.cap - KB;
+    };
+    // Compaction requests of iteration it: word it%3 collects them; word
+    // (it+1)%3 was last read before the previous barrier and is next written
+    // after this one.  After the barrier every requesting row compacts, and so
+    // does every row past half its slack.
+    auto raise_flags = [&](int it, bool need) {
+        if constexpr (kBinned) {
+            if (need && lane == 0) atomicOr(&flags[it % 3], 1);
+            if (wave == 0 && lane == 0) flags[(it + 1) % 3] = 0;
+        }
+    };
+    auto compact_if_flagged = [&](int it) {
+        if constexpr (kBinned) {
+            if (flags[it % 3] && st.cnt > want_level) {
+                compact_binned<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, st, p.topk,
+                                     p.cap, hist, bkey_all + (size_t)R * p.cap, bidx_all + (size_t)R * p.cap, lane);
+            }
+        }
+    };
+
+    // last position among this wave's valid rows (for skipping blocks)
+    const int wlast = min(i0 + wave * TW + TW, p.Lq) - 1;
+    const int wpmax = off + wlast;
+    const bool wave_has_rows = wlast >= i0 + wave * TW;
+
+    if constexpr (kPipe) {
+        // Pipelined sweep (one query of 64 heads per wavefront, 512 threads,
+        // one 16-byte chunk of each key block per thread).  Iteration blk:
+        //  * loads key block blk+2 into registers (stored to LDS an iteration later);
+        //  * reads block blk's B operands from LDS;
+        //  * phase 1: MFMAs of key fragment 0 of block blk, interleaved with the
+        //    epilogue of key fragment 1 of block blk-1;
+        //  * selection of block blk-1;
+        //  * phase 2: MFMAs of key fragment 1 of block blk, interleaved with the
+        //    epilogue of key fragment 0 of block blk;
+        //  * stores block blk+1 to LDS, barrier, batched compactions.
+        // Every epilogue reads accumulators finished a phase earlier, fragment 1's
+        // MFMAs run across the barrier, and the staging loads have two iterations
+        // to land.  Waves past their row's last block keep computing (their scores
+        // are masked by position), so the loop body has no branches around MFMAs.
+        constexpr int CPK = S::ROWB / 16;
+        static_assert(KB * CPK == kMaxThreads, "one 16-byte chunk per thread and key block");
+        const unsigned char *kseq = p.k + (size_t)b * p.Lk * S::ROWB;
+        const int krow = tid / CPK, kcol = (tid % CPK) * 16;
+        auto fetch1 = [&](int blk) {
+            const int key = min(blk * KB + krow, p.Lk - 1);   // past Lk: clamped, never used
+            return *reinterpret_cast<const v4i *>(kseq + (size_t)key * S::ROWB + kcol);
+        };
+        auto stash1 = [&](int buf, const v4i &v) {
+            *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + krow * S::PITCH + kcol) = v;
+        };
+        v4i kr[2];
+        kr[0] = fetch1(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // queries, weights and block 0
+        stash1(0, kr[0]);
+        kr[1] = fetch1(1);
+        lds_barrier();
+
+        const v16f z = {};
+        v16f a1[2] = {z, z};   // key fragment 1 of the previous block
+        float p0_prev = 0.f;   // epilogue of key fragment 0 of the previous block
+        auto combine = [](float p0, float p1) {
+            // lanes 0-31 hold key fragment 0 of their head half, lanes 32-63 the other half
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+            return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        };
+        auto iter = [&](auto PAR_, int blk) {
+            constexpr int PAR = decltype(PAR_)::value;   // == blk & 1
+            kr[PAR] = fetch1(blk + 2);
+            const unsigned char *kt = ktile + (size_t)PAR * KB * S::PITCH;
+            v8i B[2][2];
+#pragma unroll
+            for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+                for (int st2 = 0; st2 < 2; ++st2)
+                    B[cf][st2] = load32(kt + (32 * cf + (lane & 31)) * S::PITCH + 64 * st2 + 32 * (lane >> 5));
+            v16f a0[2];
+#pragma unroll
+            for (int rf = 0; rf < 2; ++rf) a0[rf] = mfma_fp8_32x32x64(Q32f.a[rf][0], B[0][0], z);
+#pragma unroll
+            for (int rf = 0; rf < 2; ++rf) a0[rf] = mfma_fp8_32x32x64(Q32f.a[rf][1], B[0][1], a0[rf]);
+            float p1 = epi32(a1[0], a1[1], Q32f);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            }
+            keep_here(p1);
+            __builtin_amdgcn_sched_barrier(0);
+            // block blk-1's selection (none before block 0: a base past every position)
+            const bool need = select_binned(combine(p0_prev, p1), blk >= 1 ? (blk - 1) * KB : INT_MAX);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rf = 0; rf < 2; ++rf) a1[rf] = mfma_fp8_32x32x64(Q32f.a[rf][0], B[1][0], z);
+#pragma unroll
+            for (int rf = 0; rf < 2; ++rf) a1[rf] = mfma_fp8_32x32x64(Q32f.a[rf][1], B[1][1], a1[rf]);
+            p0_prev = epi32(a0[0], a0[1], Q32f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            }
+            keep_here(p0_prev);
+            __builtin_amdgcn_sched_barrier(0);
+            raise_flags(blk, need);
+            // buffer PAR^1 last held block blk-1, read before the previous barrier
+            stash1(PAR ^ 1, kr[PAR ^ 1]);
+            lds_barrier();
+        };
+        // unrolled by two: one copy of the body per register buffer of the staging loads
+        for (int blk = 0; blk < nblk; blk += 2) {
+            iter(std::integral_constant<int, 0>{}, blk);
+            compact_if_flagged(blk);
+            if (blk + 1 < nblk) {
+                iter(std::integral_constant<int, 1>{}, blk + 1);
+                compact_if_flagged(blk + 1);
+            }
+        }
+        // the last block's fragment 1 and its selection (room for it was made
+        // by the last iteration's compactions)
+        (void)select_binned(combine(p0_prev, epi32(a1[0], a1[1], Q32f)), (nblk - 1) * KB);
+    } else {
     fetch(0);
     stash(0);
     // Every load issued so far (A fragments, head weights, block 0) has landed:
@@ -714,11 +870,6 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // the MFMAs never wait on them.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    // last position among this wave's valid rows (for skipping blocks)
-    const int wlast = min(i0 + wave * TW + TW, p.Lq) - 1;
-    const int wpmax = off + wlast;
-    const bool wave_has_rows = wlast >= i0 + wave * TW;
 
     for (int blk = 0; blk < nblk; ++blk) {
         const int cur = blk & 1;
@@ -804,28 +955,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
 
             // selection
             if constexpr (kBinned) {
-                const int i = i0 + wave;
-                const int pos = off + i;
-                if (i < p.Lq && base <= pos) {
-                    const int s = base + lane;
-                    if (p.scores && s < p.Lk)
-                        p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc[0] : -INFINITY;
-                    const bool cand = s <= pos && sc[0] > st.thr_f;
-                    const uint64_t m = ballot(cand);
-                    if (m) {
-                        uint32_t *bk = bkey_all + (size_t)wave * p.cap;
-                        IdxT *bi = bidx_all + (size_t)wave * p.cap;
-                        const int at = st.cnt + lanes_below(m);
-                        const uint32_t key = score_key(sc[0]);
-                        if (cand) {
-                            bk[at] = key;
-                            bi[at] = (IdxT)s;
-                        }
-                        if (st.binned) atomicAdd(&hist[cand ? bin_of(key, st.lo) : 256u + lane], 1u);
-                        st.cnt += __popcll(m);
-                    }
-                    need = st.cnt > p.cap - KB;
-                }
+                need = select_binned(sc[0], base);
             } else {
 #pragma unroll
                 for (int t = 0; t < TW; ++t) {
@@ -856,22 +986,13 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 }
             }
         }
-        if constexpr (kBinned) {
-            // word blk%3 collects this block's requests; word (blk+1)%3 was last
-            // read before the previous barrier and is next written after this one
-            if (need && lane == 0) atomicOr(&flags[blk % 3], 1);
-            if (wave == 0 && lane == 0) flags[(blk + 1) % 3] = 0;
-        }
+        raise_flags(blk, need);
         // The idle buffer was last read in block blk-1, which every wave has
         // left (barrier below); after this block's barrier it holds block blk+1.
         if (blk + 1 < nblk) stash(cur ^ 1);
         __syncthreads();
-        if constexpr (kBinned) {
-            if (flags[blk % 3] && st.cnt > want_level) {
-                compact_binned<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, st, p.topk,
-                                     p.cap, hist, bkey_all + (size_t)R * p.cap, bidx_all + (size_t)R * p.cap, lane);
-            }
-        }
+        compact_if_flagged(blk);
+    }
     }
 
     // final selection and output
@@ -1129,6 +1250,10 @@ template <Enc E, int D, int H>
 hipError_t launch_prefill_h(const IndexerArgs &a, hipStream_t st) {
     const PrefillPlan pl = plan_prefill(a);
     if (!pl.ok) return hipErrorInvalidConfiguration;
+    // the 64-head fp8 kernel with 16-bit indices runs its pipelined sweep with
+    // exactly eight wavefronts
+    if (E == Enc::FP8 && H == 64 && D == 128 && pl.idx_bytes == 2 && pl.waves * kWave != kMaxThreads)
+        return hipErrorInvalidConfiguration;
     if (pl.idx_bytes == 2) return launch_prefill_t<E, D, H, uint16_t>(a, pl.waves, pl.cap, pl.lds, st);
     return launch_prefill_t<E, D, H, uint32_t>(a, pl.waves, pl.cap, pl.lds, st);
 }

@@ -83,14 +83,6 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(const v8bf &a, const v8bf &b,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// s_waitcnt immediate for vmcnt(n) with the other counters unconstrained
-// (vmcnt is split over bits 3:0 and 15:14).
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
-// Workgroup barrier ordering LDS accesses only: the LDS-direct copies still
-// in flight are waited for with explicit vmcnt bounds, not here.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // One 8-row group rg of a tile: load Q moves line Q of the group's rows
 // (lane l: row 8rg + l/8, position l%8).  The immediate offset 128Q applies
 // to the global and to the LDS address, so the LDS base is lowered by it.
