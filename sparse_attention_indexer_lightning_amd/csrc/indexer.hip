@@ -179,6 +179,91 @@ __device__ __forceinline__ float epi32(const v16f &a0, const v16f &a1, const Q32
     return (c[0] + c[1]) + (c[2] + c[3]);
 }
 
+// The same sum with the ReLU split w*relu(x) = w*|x|/2 + w*x/2: here the
+// weights are already halved and only the |x| half is formed (one FMA with an
+// absolute-value operand per head); the linear half is added by the caller.
+__device__ __forceinline__ float epi32_abs(const v16f &a0, const v16f &a1, const Q32 &Q) {
+    float c[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        c[h] = Q.w[0][8 * h] * fabsf(a0[8 * h]);
+        c[2 + h] = Q.w[1][8 * h] * fabsf(a1[8 * h]);
+#pragma unroll
+        for (int r = 1; r < 8; ++r) {
+            c[h] = __builtin_fmaf(Q.w[0][8 * h + r], fabsf(a0[8 * h + r]), c[h]);
+            c[2 + h] = __builtin_fmaf(Q.w[1][8 * h + r], fabsf(a1[8 * h + r]), c[2 + h]);
+        }
+    }
+    return (c[0] + c[1]) + (c[2] + c[3]);
+}
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// Linear half of the score for four queries (4jq .. 4jq+3 of the workgroup's
+// rows): sum_h (w_h/2) (q_h . k) = qw . k with qw = sum_h (w_h/2) q_h.  qw is
+// formed in fp32, scaled by S = 2^e (max_d |qw[d]| S in [128, 256)) and split
+// into four fp8 e4m3 terms: term j = rne(r_j 16^j), r_0 = qw S and r_{j+1} =
+// r_j - term_j 16^-j (exact in fp32), so sum_j term_j 16^-j = qw S to about
+// 2^-16 relative.  Returns the A fragment of a 16x16x128 fp8 MFMA whose row
+// r = l%16 is query 4jq + r/4, term r%4 (d = 32(l/16)..+31), and sets inv_s to
+// 1/S of query 4jq + l/16, the one whose row block lane l receives.
+__device__ v8i linear_terms_frag(const unsigned char *q, const void *w, Enc w_enc, size_t row0, int nrows,
+                                 int jq, int lane, float &inv_s) {
+    constexpr int H = 64, ROWB = 128;
+    const int r = lane & 15, tq = 4 * jq + (r >> 2), kq = lane & 3, dr = 32 * (lane >> 4);
+    // each lane of a quad sums 8 of the quad's 32 dimensions over the heads
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (tq < nrows) {
+        const size_t qi = row0 + tq;
+        const unsigned char *qp = q + qi * H * ROWB + dr + 8 * kq;
+        for (int h = 0; h < H; ++h) {
+            const float wh = 0.5f * load_w(w, w_enc, qi * H + h);
+            const v2i qb = *reinterpret_cast<const v2i *>(qp + (size_t)h * ROWB);
+            const v2f f[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(qb[0], false), __builtin_amdgcn_cvt_pk_f32_fp8(qb[0], true),
+                              __builtin_amdgcn_cvt_pk_f32_fp8(qb[1], false), __builtin_amdgcn_cvt_pk_f32_fp8(qb[1], true)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = __builtin_fmaf(wh, f[e][0], acc[2 * e]);
+                acc[2 * e + 1] = __builtin_fmaf(wh, f[e][1], acc[2 * e + 1]);
+            }
+        }
+    }
+    float v[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * k + e] = __shfl(acc[e], (lane & ~3) | k, kWave);
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) m = fmaxf(m, fabsf(v[e]));
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    const int ex = m > 0.f ? 8 - __builtin_amdgcn_frexp_expf(m) : 0;
+    const float sc = __builtin_amdgcn_ldexpf(1.f, ex);
+    v8i a;
+#pragma unroll
+    for (int e = 0; e < 32; e += 2) {
+        float pick[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float rr = v[e + u] * sc;
+            pick[u] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x = rr * __builtin_amdgcn_ldexpf(1.f, 4 * j);
+                if (j == kq) pick[u] = x;
+                const int enc = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false);
+                rr -= __builtin_amdgcn_cvt_f32_fp8(enc, 0) * __builtin_amdgcn_ldexpf(1.f, -4 * j);
+            }
+        }
+        if (e & 2) a[e >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(pick[0], pick[1], a[e >> 2], true);
+        else a[e >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(pick[0], pick[1], 0, false);
+    }
+    inv_s = __shfl(__builtin_amdgcn_ldexpf(1.f, -ex), 4 * (lane >> 4), kWave);
+    return a;
+}
+
 // Scores of 64 keys for one query from the lane's B pieces B[cf][st]:
 // key 32cf + l%32, d = 64st + 32(l/32) .. +31.  Lane l gets key l.
 __device__ __forceinline__ float score64_mfma32_b(const Q32 &Q, const v8i (&B)[2][2]) {
@@ -590,13 +675,16 @@ struct PrefillLds {
     size_t ktile, stage, hist, flags, state, bkey, bidx, total;
 };
 
-__host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, int cap, int idx_bytes, bool staged) {
+// `stage` holds one score per (row, key of a block): once for the staged
+// kernels (H < 16), twice (by block parity) for the linear score terms of the
+// pipelined 64-head kernel.
+__host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, int cap, int idx_bytes, int stage_bufs) {
     PrefillLds L;
     const int R = waves * tw;
     L.ktile = 0;
     size_t off = (size_t)2 * KB * pitch;
     L.stage = off;
-    off += staged ? (size_t)waves * tw * KB * 4 : 0;
+    off += (size_t)stage_bufs * waves * tw * KB * 4;
     L.hist = off;
     off += (size_t)waves * kHistWords * 4;
     L.flags = off;
@@ -618,12 +706,16 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     constexpr int TW = 64 / H;              // query rows per wave
     constexpr bool kStaged = H < 16;        // scores go through LDS before selection
     constexpr bool kBinned = TW == 1;       // binned selection + batched compaction
+    constexpr bool kMfma32 = E == Enc::FP8 && H == 64 && D == 128;
+    // the pipelined sweep below needs eight wavefronts, which the LDS plan
+    // always gives with 16-bit candidate indices (keys up to 65536)
+    constexpr bool kPipe = kMfma32 && sizeof(IdxT) == 2;
     const int waves = p.nthreads / kWave;
     const int R = waves * TW;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4, n = lane & 15;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    const PrefillLds L = prefill_lds(waves, TW, S::PITCH, p.cap, (int)sizeof(IdxT), kStaged);
+    const PrefillLds L = prefill_lds(waves, TW, S::PITCH, p.cap, (int)sizeof(IdxT), kStaged ? 1 : kPipe ? 2 : 0);
     unsigned char *ktile = smem + L.ktile;
     float *stage = reinterpret_cast<float *>(smem + L.stage) + (size_t)wave * TW * KB;
     uint32_t *hist = reinterpret_cast<uint32_t *>(smem + L.hist) + wave * kHistWords;
@@ -642,10 +734,6 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int pmax = off + min(i0 + R, p.Lq) - 1;
     const int nblk = pmax / KB + 1;
 
-    constexpr bool kMfma32 = E == Enc::FP8 && H == 64 && D == 128;
-    // the pipelined sweep below needs eight wavefronts, which the LDS plan
-    // always gives with 16-bit candidate indices (keys up to 65536)
-    constexpr bool kPipe = kMfma32 && sizeof(IdxT) == 2;
     Q32 Q32f;
     if constexpr (kMfma32) {
         const int i = i0 + wave;
@@ -654,6 +742,12 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             load_q32(Q32f, p.q + qi * H * S::ROWB, [&](int h) { return load_w(p.w, p.w_enc, qi * H + h); }, lane);
         } else {
             load_q32(Q32f, p.q, [&](int h) { return 0.f; }, lane);
+        }
+        if constexpr (kPipe) {
+#pragma unroll
+            for (int rf = 0; rf < 2; ++rf)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Q32f.w[rf][r] *= 0.5f;   // ReLU split: w*|x|/2 + w*x/2
         }
     }
     // A fragments: fragment f, row r = 16f + n -> (t, h) = (r / H, r % H)
@@ -778,6 +872,19 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         // MFMAs run across the barrier, and the staging loads have two iterations
         // to land.  Waves past their row's last block keep computing (their scores
         // are masked by position), so the loop body has no branches around MFMAs.
+        //
+        // The epilogue uses the ReLU split w*relu(x) = w*|x|/2 + w*x/2: one FMA on
+        // |x| per (head, key), while the linear half of all eight rows' scores,
+        // qw.k per row (qw = sum_h (w_h/2) q_h), takes one 16x16x128 fp8 MFMA per
+        // wavefront and block: wavefront v covers rows 4(v%2)..+3 and keys
+        // 16(v/2)..+15 of the block and leaves them in LDS (by block parity) for
+        // the owning rows' selection an iteration later.
+        const int jq = wave & 1, sq = wave >> 1;
+        float inv_s_lin;
+        const v8i Alin = linear_terms_frag(p.q, p.w, p.w_enc, (size_t)b * p.Lq + i0, p.Lq - i0, jq, lane, inv_s_lin);
+        float *linbuf = reinterpret_cast<float *>(smem + L.stage);   // [2][8 rows][64 keys]
+        const int lin_put = (4 * jq + (lane >> 4)) * KB + 16 * sq + (lane & 15);
+        const int lin_get = wave * KB + lane;
         constexpr int CPK = S::ROWB / 16;
         static_assert(KB * CPK == kMaxThreads, "one 16-byte chunk per thread and key block");
         const unsigned char *kseq = p.k + (size_t)b * p.Lk * S::ROWB;
@@ -814,34 +921,40 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
                 for (int st2 = 0; st2 < 2; ++st2)
                     B[cf][st2] = load32(kt + (32 * cf + (lane & 31)) * S::PITCH + 64 * st2 + 32 * (lane >> 5));
+            const v8i Bl = load32(kt + (16 * sq + (lane & 15)) * S::PITCH + 32 * (lane >> 4));
+            const v4f dl = mfma_fp8_16x16x128(Alin, Bl, v4f{0.f, 0.f, 0.f, 0.f});
             v16f a0[2];
 #pragma unroll
             for (int rf = 0; rf < 2; ++rf) a0[rf] = mfma_fp8_32x32x64(Q32f.a[rf][0], B[0][0], z);
 #pragma unroll
             for (int rf = 0; rf < 2; ++rf) a0[rf] = mfma_fp8_32x32x64(Q32f.a[rf][1], B[0][1], a0[rf]);
-            float p1 = epi32(a1[0], a1[1], Q32f);
+            float p1 = epi32_abs(a1[0], a1[1], Q32f);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 5; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
             }
             keep_here(p1);
             __builtin_amdgcn_sched_barrier(0);
             // block blk-1's selection (none before block 0: a base past every position)
-            const bool need = select_binned(combine(p0_prev, p1), blk >= 1 ? (blk - 1) * KB : INT_MAX);
+            const float lin_prev = linbuf[(PAR ^ 1) * (8 * KB) + lin_get];
+            const bool need = select_binned(combine(p0_prev, p1) + lin_prev, blk >= 1 ? (blk - 1) * KB : INT_MAX);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rf = 0; rf < 2; ++rf) a1[rf] = mfma_fp8_32x32x64(Q32f.a[rf][0], B[1][0], z);
 #pragma unroll
             for (int rf = 0; rf < 2; ++rf) a1[rf] = mfma_fp8_32x32x64(Q32f.a[rf][1], B[1][1], a1[rf]);
-            p0_prev = epi32(a0[0], a0[1], Q32f);
+            p0_prev = epi32_abs(a0[0], a0[1], Q32f);
+            // the four split terms, rescaled (exact powers of two) and summed
+            const float lin = (((dl[3] * 0.0625f + dl[2]) * 0.0625f + dl[1]) * 0.0625f + dl[0]) * inv_s_lin;
+            linbuf[PAR * (8 * KB) + lin_put] = lin;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
             }
             keep_here(p0_prev);
             __builtin_amdgcn_sched_barrier(0);
@@ -861,7 +974,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         }
         // the last block's fragment 1 and its selection (room for it was made
         // by the last iteration's compactions)
-        (void)select_binned(combine(p0_prev, epi32(a1[0], a1[1], Q32f)), (nblk - 1) * KB);
+        (void)select_binned(combine(p0_prev, epi32_abs(a1[0], a1[1], Q32f)) + linbuf[((nblk - 1) & 1) * (8 * KB) + lin_get],
+                            (nblk - 1) * KB);
     } else {
     fetch(0);
     stash(0);
@@ -1219,13 +1333,15 @@ PrefillPlan plan_prefill(const IndexerArgs &a) {
     const int tw = 64 / a.H;
     const bool staged = a.H < 16;
     pl.idx_bytes = a.Lk <= 65536 ? 2 : 4;
+    const bool pipe = a.qk_enc == Enc::FP8 && a.H == 64 && a.D == 128 && pl.idx_bytes == 2;
+    const int stage_bufs = staged ? 1 : pipe ? 2 : 0;
     const int nchunk = KB * rowb / 16;
     int min_waves = (nchunk + kChunkMax * kWave - 1) / (kChunkMax * kWave);
     if (min_waves < 1) min_waves = 1;
     for (int waves = 8; waves >= min_waves; waves /= 2) {
         // room beyond k: at least two blocks of appends; more room means fewer
         // compactions per row.  Take the most LDS allows (multiple of 64, <= 2048).
-        const PrefillLds base = prefill_lds(waves, tw, pitch, 0, pl.idx_bytes, staged);
+        const PrefillLds base = prefill_lds(waves, tw, pitch, 0, pl.idx_bytes, stage_bufs);
         if (base.total + 64 > kLdsBudget) {
             if (waves == 1) break;
             continue;
@@ -1237,7 +1353,7 @@ PrefillPlan plan_prefill(const IndexerArgs &a) {
         if (cap >= a.topk + 2 * KB) {
             pl.waves = waves;
             pl.cap = (int)cap;
-            pl.lds = prefill_lds(waves, tw, pitch, pl.cap, pl.idx_bytes, staged).total;
+            pl.lds = prefill_lds(waves, tw, pitch, pl.cap, pl.idx_bytes, stage_bufs).total;
             pl.ok = pl.lds <= kLdsBudget;
             if (pl.ok) return pl;
         }

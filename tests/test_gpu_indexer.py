@@ -151,7 +151,12 @@ def test_determinism():
 
 
 def test_fused_and_split_paths_agree():
-    """The fused prefill kernel and the split-key path select the same sets."""
+    """The fused prefill kernel and the split-key path agree: the same queries
+    scored by both give scores within the score tolerance of each other and
+    index sets that differ only at keys within it of the k-th score.  (The two
+    kernels sum in different fp32 orders: the 64-head fused kernel splits the
+    ReLU as w*|x|/2 + w*x/2 with the linear half on an MFMA, so their scores are
+    not bit-identical.)"""
     wl = inputs.Workload("a", 2, 4, 6000, 64, 128, 700, "fp8", "bf16", 12)
     q, k, w = inputs.indexer_inputs(wl, 0, DEV)
     t_split, s_split = run_full(q, k, w, 700)           # Lq <= 4: split-key path
@@ -162,6 +167,10 @@ def test_fused_and_split_paths_agree():
     q2[:, 36:] = q
     w2[:, 36:] = w
     t_fused, s_fused = run_full(q2.contiguous(), k, w2.contiguous(), 700)
-    assert torch.equal(t_split, t_fused[:, 36:])
-    assert torch.equal(s_split, s_fused[:, 36:])
+    sg = s_fused[:, 36:].cpu().numpy().reshape(8, -1)
+    so = s_split.cpu().numpy().reshape(8, -1).astype(np.float64)
+    check_scores(sg, so, RTOL["fp8"], "fused vs split")
+    pos = oracle.row_positions(2, 4, 6000)
+    check_index_sets(t_fused[:, 36:].cpu().numpy().reshape(8, -1), t_split.cpu().numpy().reshape(8, -1), so, pos,
+                     700, RTOL["fp8"], "fused vs split")
     del wl2
