@@ -14,24 +14,25 @@
 // index set is split into chunks that run as separate workgroups, and a second
 // kernel merges their normalised partial outputs by log-sum-exp weights.
 //
-// Workgroup: one query, 64 heads, one chunk of the index set; 4 wavefronts
-// in two roles that run one tile apart:
+// Workgroup: one query, 64 heads, one chunk of the index set; 8 wavefronts
+// in two roles that run one tile apart, one of each role per SIMD:
 //  * Rows are consumed in tiles of 32.  Tiles are copied straight from HBM
 //    into a ring of four LDS slots with LDS-direct 16-byte loads, two tiles
 //    ahead; the index values that drive the copies are themselves copied
-//    into a small LDS ring four tiles ahead.  All wavefronts copy.
-//  * Producers (wavefronts 0, 1; heads 32p..32p+31): S^T = K Q^T for the 32
-//    rows of tile s on 32x32x16 bf16 MFMA, query fragments held in registers
-//    for the whole sweep; the softmax probabilities go to LDS in bf16.  Each
-//    head's reference is raised lazily, only when a tile's maximum exceeds it
-//    by more than kSlack (log2 units), and the producer that owns the head
-//    publishes the rescale factor with the probabilities.
-//  * Consumers (wavefronts 2, 3; output columns 256c..256c+255 of all 64
-//    heads): O^T += V^T P^T for tile s-1, V^T read with transposing LDS loads;
-//    a published rescale is applied before the tile it belongs to.
+//    into a small LDS ring four tiles ahead.  The consumers copy.
+//  * Producers (wavefronts 0-3; heads 16p..16p+15): S = K Q^T for the 32 rows
+//    of tile s on 16x16x32 bf16 MFMA, query fragments held in AGPRs for the
+//    whole sweep; the softmax probabilities go to LDS in bf16.  Each head's
+//    reference is raised lazily, only when a tile's maximum exceeds it by more
+//    than kSlack (log2 units), and the producer publishes the rescale factor
+//    with the probabilities.
+//  * Consumers (wavefronts 4-7; output columns 128c..128c+127 of all 64
+//    heads): O^T += V^T P^T for tile s-1, V^T read with transposing LDS
+//    loads; a published rescale is applied before the tile it belongs to.
 //  * One workgroup barrier per tile.  The two roles are separate code paths,
 //    so the query fragments (producers) and the output accumulators
-//    (consumers) never need registers in the same wavefront.
+//    (consumers) never need registers in the same wavefront; both sit in the
+//    AGPR file, which VGPRs and AGPRs being budgeted per kernel requires.
 #include <algorithm>
 #include <type_traits>
 
@@ -49,14 +50,14 @@ constexpr int ROWB = DQK * 2;                 // bytes per latent row
 constexpr int OCTETS = ROWB / 128;            // 128-byte lines per row
 constexpr int OCT_BYTES = RT * 128;           // one line of every row of a tile
 constexpr int SLOT = OCTETS * OCT_BYTES;      // bytes per tile
-constexpr int WAVES = 4;
-constexpr int KS = DQK / 16;                  // logit k-steps
+constexpr int WAVES = 8;                      // 4 producers, 4 consumers
+constexpr int KS = DQK / 32;                  // logit k-steps (16x16x32 MFMA)
 constexpr int RING = 8;                       // index ring, in tiles
 constexpr int PB = HW * RT * 2;               // probability tile, bf16 [head][row]
 constexpr float kSlack = 8.f;
 static_assert(ROWB % 128 == 0, "rows are whole 128-byte lines");
-static_assert(RT == 8 * WAVES, "each wavefront copies one 8-row group");
-static_assert(HW == 64 && DV == 512, "two producers of 32 heads, two consumers of 256 columns");
+static_assert(RT == 8 * 4, "each consumer copies one 8-row group");
+static_assert(HW == 64 && DV == 512 && RT == 32, "four producers of 16 heads, four consumers of 128 columns");
 
 // Slot layout: line-major [line q][row r][position], where 16-byte piece
 // 8q + p of row r sits at position (p + f(r)) mod 8.  f makes the two LDS
@@ -99,6 +100,15 @@ __device__ __forceinline__ float swap32_max(float v) {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
+// maxima and sums over lanes l and l^16 (the 16-lane rows swapped pairwise)
+__device__ __forceinline__ float swap16_max(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float swap16_sum(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
 __device__ __forceinline__ float swap32_sum(float v) {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -126,7 +136,7 @@ struct Smem {
     unsigned char ptile[2][PB];               // [tile parity] bf16 [head][4 chunks of 8 rows]
     int ring[RING][RT];                       // index values of tiles t % RING
     float alpha[2][HW];                       // [tile parity] rescale factor per head
-    int flag[2][2];                           // [tile parity][producer] some head was rescaled
+    int flag[2][4];                           // [tile parity][producer] some head was rescaled
     float lsum[HW], mref[HW];
 };
 
@@ -167,10 +177,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
     if (tid < 4 * RT) sm.ring[tid / RT][tid % RT] = trow[min(cs + tid, a.topk - 1)];
     lds_barrier();
 
-    // Copies are issued by the two consumer wavefronts only (consumer c
-    // copies row groups 2c and 2c+1 of every tile), so that the producers,
-    // which set the pace, spend no issue slots on them.  Lane l of a group
-    // copy moves position l%8 of row 8rg + l/8.
+    // Copies are issued by the consumer wavefronts only (consumer c copies
+    // row group c of every tile), so that the producers, which set the pace,
+    // spend no issue slots on them.  Lane l of a group copy moves position
+    // l%8 of row 8rg + l/8.
     auto copy_group = [&](lds_u8 *slot, int t, int ix, int rg) {
         const int row = 8 * rg + (lane >> 3);
         const bool ok = RT * t + row < clen && ix >= 0 && ix < a.Lk;
@@ -192,22 +202,30 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
         if (s + 2 <= ntiles) step(std::integral_constant<int, 2>{}, s + 2);
     };
 
-    if (wave < 2) {
-        // ---------------- producer: logits and probabilities of heads 32p..32p+31
+    if (wave < 4) {
+        // ---------------- producer: heads 16p..16p+15, all rows of each tile
         const int p = wave;
-        const int H = 32 * p + n;                 // head (within the block) of this lane
+        const int n16 = lane & 15, g = lane >> 4;
+        const int H = 16 * p + n16;               // head (within the block) of this lane
         const float sl2 = a.sm_scale * 1.4426950408889634f;
-        v4i qf[KS];                               // B operand: head h0 + H, piece 2c + hh
+        v4i qf[KS];                               // B operand: head H, d = 32ks + 8g..+7
         {
-            const v4i *qh = reinterpret_cast<const v4i *>(static_cast<const unsigned char *>(a.q) +
-                                                          ((size_t)qrow * a.Hq + h0 + H) * ROWB);
+            const unsigned char *qh = static_cast<const unsigned char *>(a.q) + ((size_t)qrow * a.Hq + h0 + H) * ROWB;
 #pragma unroll
-            for (int c = 0; c < KS; ++c) qf[c] = qh[2 * c + hh];
+            for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const v4i *>(qh + 64 * ks + 16 * g);
+            // the query fragments live in AGPRs (MFMA operands may come from
+            // either file): VGPRs and AGPRs are allocated per kernel, and the
+            // consumers' output accumulators fill the AGPR budget anyway
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(qf[ks]));
         }
-        // A operand: row n of the tile, piece 2c + hh = line c/4, piece 2(c%4) + hh
-        int kb[4];
+        // A operand of k-step ks, row block rb: row 16rb + n16 of the tile,
+        // 16-byte piece 4ks + g = line ks/2, piece 4(ks%2) + g
+        int kb[2][2];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) kb[k] = 128 * n + 16 * pos_of(2 * k + hh, n);
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) kb[rb][k] = 128 * (16 * rb + n16) + 16 * pos_of(4 * k + g, 16 * rb + n16);
         float m_ref = -INFINITY, l_lane = 0.f;
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // query fragments
         lds_barrier();   // tile 0 landed (consumers' copies)
@@ -215,70 +233,83 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
         auto step = [&](auto PI_, int s) {
             constexpr int PI = decltype(PI_)::value;
             lds_u8 *cur = SL(std::integral_constant<int, PI>{});
+            const int par = s & 1;
             const int ix_mask_next = sm.ring[(s + 1) & (RING - 1)][n];
             if (s < ntiles) {
-                int kbs[4];
+                int kbs[2][2];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) kbs[k] = opaque(kb[k]);
-                // software pipeline over groups of four k-steps: the reads of
-                // group g+1 are in flight while group g runs on the MFMA unit
-                v16f sacc = v16f{};
-                v4i kf[2][4];
+                for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) kf[0][i] = lds_read_b128(cur + kbs[i] + OCT_BYTES * 0);
+                    for (int k = 0; k < 2; ++k) kbs[rb][k] = opaque(kb[rb][k]);
+                // software pipeline over pairs of k-steps: the reads of pair
+                // q+1 are in flight while pair q runs on the MFMA unit
+                v4f acc[2];
+                acc[0] = v4f{0.f, 0.f, 0.f, 0.f};
+                acc[1] = acc[0];
+                v4i kf[2][2][2];   // [buffer][k-step of the pair][row block]
 #pragma unroll
-                for (int g = 0; g < KS / 4; ++g) {
-                    if (g + 1 < KS / 4) {
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) kf[(g + 1) & 1][i] = lds_read_b128(cur + kbs[i] + OCT_BYTES * (g + 1));
+                    for (int rb = 0; rb < 2; ++rb) kf[0][i][rb] = lds_read_b128(cur + kbs[rb][i & 1] + OCT_BYTES * (i >> 1));
+#pragma unroll
+                for (int q = 0; q < KS / 2; ++q) {
+                    if (q + 1 < KS / 2) {
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const int ks = 2 * (q + 1) + i;
+#pragma unroll
+                            for (int rb = 0; rb < 2; ++rb)
+                                kf[(q + 1) & 1][i][rb] = lds_read_b128(cur + kbs[rb][ks & 1] + OCT_BYTES * (ks >> 1));
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        sacc = mfma_bf16_32x32x16(__builtin_bit_cast(v8bf, kf[g & 1][i]), __builtin_bit_cast(v8bf, qf[4 * g + i]), sacc);
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int rb = 0; rb < 2; ++rb)
+                            acc[rb] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, kf[q & 1][i][rb]),
+                                                         __builtin_bit_cast(v8bf, qf[2 * q + i]), acc[rb]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                // rows of this lane: 8i + 4hh + j for register 4i + j; logits
-                // stay unscaled (z * sl2 is formed inside the exponent)
+                // rows of this lane: 16rb + 4g + i for register i of block rb;
+                // logits stay unscaled (z * sl2 is formed inside the exponent)
                 const bool vrow = RT * s + n < clen && ix_mask >= 0 && ix_mask < a.Lk;
-                const uint64_t vball = ballot(vrow && hh == 0);
-                const bool all_valid = (uint32_t)vball == 0xFFFFFFFFu;
+                const uint32_t vball = (uint32_t)ballot(vrow && hh == 0);   // bit r: row r
+                const bool all_valid = vball == 0xFFFFFFFFu;
                 float lm = -INFINITY;
-                if (all_valid) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) lm = fmaxf(lm, sacc[r]);
-                } else {
-                    const uint32_t vmask = (uint32_t)vball >> (4 * hh);
+                for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        sacc[r] = ((vmask >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] : -INFINITY;
-                        lm = fmaxf(lm, sacc[r]);
+                    for (int i = 0; i < 4; ++i) {
+                        if (!all_valid) acc[rb][i] = ((vball >> (16 * rb + 4 * g + i)) & 1u) ? acc[rb][i] : -INFINITY;
+                        lm = fmaxf(lm, acc[rb][i]);
                     }
-                }
-                lm = swap32_max(lm) * sl2;   // sl2 > 0: the maximum of the scaled logits
+                lm = swap32_max(swap16_max(lm)) * sl2;   // sl2 > 0: the maximum of the scaled logits
                 const float m_new = lm > m_ref + kSlack ? lm : m_ref;
                 const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                const int par = s & 1;
-                if (hh == 0) sm.alpha[par][H] = alpha;
+                if (g == 0) sm.alpha[par][H] = alpha;
                 const bool raised = ballot(m_new != m_ref) != 0;
                 if (lane == 0) sm.flag[par][p] = raised ? 1 : 0;
-                float ps = 0.f;
-                lds_u8 *pt = (lds_u8 *)sm.ptile[par] + 64 * H + 8 * hh;
                 // exp2(-inf) = 0 takes care of masked rows whenever m_new is
                 // finite; m_new = -inf means no valid row so far (all zero)
                 const float mneg = m_new == -INFINITY ? 0.f : -m_new;
+                lds_u8 *ptp = (lds_u8 *)sm.ptile[par];
+                float ps = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int rb = 0; rb < 2; ++rb) {
                     float pv[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * i + j], sl2, mneg));
-                        ps += pv[j];
+                    for (int i = 0; i < 4; ++i) {
+                        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[rb][i], sl2, mneg));
+                        ps += pv[i];
                     }
+                    // rows 16rb + 4g..+3: half g%2 of chunk q = 2rb + g/2, chunk q
+                    // of head H stored at 16((q + H/4) mod 4)
                     v2i w2;
                     w2[0] = (int)pack_bf16(pv[0], pv[1]);
                     w2[1] = (int)pack_bf16(pv[2], pv[3]);
-                    lds_write_b64(pt + 16 * ((i + (H >> 2)) & 3), w2);
+                    const int q = 2 * rb + (g >> 1);
+                    lds_write_b64(ptp + 64 * H + 16 * ((q + (H >> 2)) & 3) + 8 * (g & 1), w2);
                 }
                 l_lane = l_lane * alpha + ps;
                 m_ref = m_new;
@@ -287,19 +318,19 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
             ix_mask = ix_mask_next;
         };
         run(step);
-        const float l_head = swap32_sum(l_lane);
-        if (hh == 0) {
+        const float l_head = swap32_sum(swap16_sum(l_lane));
+        if (g == 0) {
             sm.lsum[H] = l_head;
             sm.mref[H] = m_ref;
         }
         lds_barrier();   // statistics visible
         lds_barrier();   // consumers staged the output
     } else {
-        // ---------------- consumer: output columns 256c..256c+255 of all 64 heads
-        const int c = wave - 2;
+        // ---------------- consumer: output columns 128c..128c+127 of all 64 heads
+        const int c = wave - 4;
         // transposed V reads: lane (G = lane/16, j = (lane/4)%4, cc = lane%4) ->
-        // row 8(G/2) + 4t + j, columns 256c + 32mb + 16(G%2) + 4cc..+3 = line
-        // 4c + mb/2, piece 4(mb%2) + 2(G%2) + cc/2, byte 8(cc%2)
+        // row 8(G/2) + 4t + j, columns 128c + 32mb + 16(G%2) + 4cc..+3 = line
+        // 2c + mb/2, piece 4(mb%2) + 2(G%2) + cc/2, byte 8(cc%2)
         int vb[2][2];
         {
             const int G = lane >> 4, j = (lane >> 2) & 3, cc = lane & 3;
@@ -308,7 +339,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int r = 8 * (G >> 1) + 4 * t + j;
-                    vb[m2][t] = OCT_BYTES * 4 * c + 128 * r + 16 * pos_of(4 * m2 + 2 * (G & 1) + (cc >> 1), r) + 8 * (cc & 1);
+                    vb[m2][t] = OCT_BYTES * 2 * c + 128 * r + 16 * pos_of(4 * m2 + 2 * (G & 1) + (cc >> 1), r) + 8 * (cc & 1);
                 }
         }
         // B operand of k-step cp: head 32nb + n, rows 16cp + 8hh..+7 = chunk
@@ -316,51 +347,51 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
         int pbase[2];
 #pragma unroll
         for (int cp = 0; cp < 2; ++cp) pbase[cp] = 64 * n + 16 * ((2 * cp + hh + (n >> 2)) & 3);
-        v16f o[8][2];
+        v16f o[4][2];
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) o[mb][nb] = v16f{};
-        // index values of tile t for rows 16c..16c+15 (lane l holds row
-        // 16c + l%16), loaded by every lane so that each step issues the same
-        // number of vector-memory operations whatever the lane mask
-        auto load_index = [&](int t) -> int { return trow[min(cs + RT * t + 16 * c + (lane & 15), a.topk - 1)]; };
-        const int crow0 = 16 * c + (lane >> 3), crow1 = crow0 + 8;   // copy rows of groups 2c, 2c+1
-        int pend = load_index(4);
-        copy_group(SL(std::integral_constant<int, 0>{}), 0, sm.ring[0][crow0], 2 * c);
-        copy_group(SL(std::integral_constant<int, 0>{}), 0, sm.ring[0][crow1], 2 * c + 1);
-        copy_group(SL(std::integral_constant<int, 1>{}), 1, sm.ring[1][crow0], 2 * c);
-        copy_group(SL(std::integral_constant<int, 1>{}), 1, sm.ring[1][crow1], 2 * c + 1);
-        int ix0 = sm.ring[2][crow0], ix1 = sm.ring[2][crow1];
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OCTETS));   // the index load and tile 0 landed
+        // index values of tile t for rows 8c..8c+7 (lane l holds row 8c + l%8),
+        // loaded by every lane so that each step issues the same number of
+        // vector-memory operations whatever the lane mask
+        auto load_index = [&](int t) -> int { return trow[min(cs + RT * t + 8 * c + (lane & 7), a.topk - 1)]; };
+        const int crow = 8 * c + (lane >> 3);   // copy row of group c
+        // index loads by step parity (moving a register whose load is in
+        // flight would wait for it)
+        int pendb[2] = {0, load_index(4)};
+        copy_group(SL(std::integral_constant<int, 0>{}), 0, sm.ring[0][crow], c);
+        copy_group(SL(std::integral_constant<int, 1>{}), 1, sm.ring[1][crow], c);
+        int ix = sm.ring[2][crow];
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(OCTETS));   // the index load and tile 0 landed
         lds_barrier();
-        // step s starts with the load of the indices of tile s+5 and the
-        // copy of tile s+2 (19 vector-memory operations); it ends by waiting
-        // for tile s+1 and the indices of tile s+4, which then go to the ring
+        // step s starts with the load of the indices of tile s+5 and the copy
+        // of tile s+2 (10 vector-memory operations); it ends by waiting for
+        // tile s+1 and the indices of tile s+4, which then go to the ring.  The
+        // products of tile s-1 run after barrier A, while the producers work
+        // on the softmax of tile s.
         auto step = [&](auto PI_, int s) {
             constexpr int PI = decltype(PI_)::value;
             lds_u8 *prv = SL(std::integral_constant<int, PI + 3>{});
             lds_u8 *nx2 = SL(std::integral_constant<int, PI + 2>{});   // held tile s-2, consumed before the last barrier
-            const int pend_next = load_index(s + 5);
-            copy_group(nx2, s + 2, ix0, 2 * c);
-            copy_group(nx2, s + 2, ix1, 2 * c + 1);
-            const int ix0_next = sm.ring[(s + 3) & (RING - 1)][crow0];
-            const int ix1_next = sm.ring[(s + 3) & (RING - 1)][crow1];
-            if (s >= 1) {
-                const int par = (s - 1) & 1;
-                if (sm.flag[par][0] | sm.flag[par][1]) {
-                    // a reference of tile s-1 was raised: rescale tiles 0..s-2
+            pendb[PI & 1] = load_index(s + 5);
+            copy_group(nx2, s + 2, ix, c);
+            const int ix_next = sm.ring[(s + 3) & (RING - 1)][crow];
+            const int par = (s - 1) & 1;
+            if (s >= 1 && (sm.flag[par][0] | sm.flag[par][1] | sm.flag[par][2] | sm.flag[par][3])) {
+                // a reference of tile s-1 was raised: rescale tiles 0..s-2
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
-                        const float al = sm.alpha[par][32 * nb + n];
+                for (int nb = 0; nb < 2; ++nb) {
+                    const float al = sm.alpha[par][32 * nb + n];
 #pragma unroll
-                        for (int mb = 0; mb < 8; ++mb) {
-                            pin_acc(o[mb][nb]);
-                            o[mb][nb] *= al;
-                            pin_acc(o[mb][nb]);
-                        }
+                    for (int mb = 0; mb < 4; ++mb) {
+                        pin_acc(o[mb][nb]);
+                        o[mb][nb] *= al;
+                        pin_acc(o[mb][nb]);
                     }
                 }
+            }
+            if (s >= 1) {
                 int vbs[2][2], pbs[2];
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2)
@@ -369,43 +400,40 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
 #pragma unroll
                 for (int cp = 0; cp < 2; ++cp) pbs[cp] = opaque(pbase[cp]);
                 // two batches, one per k-step of 16 rows: all V^T and P^T
-                // operands of a batch are read at once.  The consumer has LDS
-                // copies in flight, so every wait for an LDS read is a full
-                // one; batching leaves one exposed wait per tile, and the
-                // second batch's reads complete under the first batch's MFMAs.
-                auto read_batch = [&](int cp, v8bf (&va)[8], v8bf (&pb)[2]) {
+                // operands of a batch are read at once; the second batch's
+                // reads complete under the first batch's MFMAs
+                auto read_batch = [&](int cp, v8bf (&va)[4], v8bf (&pb)[2]) {
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb)
                         pb[nb] = __builtin_bit_cast(v8bf, lds_read_b128((lds_u8 *)sm.ptile[par] + pbs[cp] + 2048 * nb));
 #pragma unroll
-                    for (int mb = 0; mb < 8; ++mb) {
+                    for (int mb = 0; mb < 4; ++mb) {
                         const v4s lo = lds_read_tr16(prv + vbs[mb & 1][0] + OCT_BYTES * (mb >> 1) + 2048 * cp);
                         const v4s hi = lds_read_tr16(prv + vbs[mb & 1][1] + OCT_BYTES * (mb >> 1) + 2048 * cp);
                         va[mb] = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     }
                 };
-                v8bf va0[8], va1[8], pb0[2], pb1[2];
+                v8bf va0[4], va1[4], pb0[2], pb1[2];
                 read_batch(0, va0, pb0);
                 __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): batch 0 landed
                 __builtin_amdgcn_sched_barrier(0);
                 read_batch(1, va1, pb1);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mb = 0; mb < 8; ++mb)
+                for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma_bf16_32x32x16(va0[mb], pb0[nb], o[mb][nb]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mb = 0; mb < 8; ++mb)
+                for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma_bf16_32x32x16(va1[mb], pb1[nb], o[mb][nb]);
             }
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OCTETS + 1));
-            if (lane < 16) sm.ring[(s + 4) & (RING - 1)][16 * c + lane] = pend;
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(OCTETS + 1));
+            const int pend = pendb[(PI & 1) ^ 1];   // indices of tile s+4 (landed)
+            if (lane < 8) sm.ring[(s + 4) & (RING - 1)][8 * c + lane] = pend;
             lds_barrier();
-            pend = pend_next;
-            ix0 = ix0_next;
-            ix1 = ix1_next;
+            ix = ix_next;
         };
         run(step);
         // the copies past the last tile may still be in flight: let them
@@ -421,11 +449,11 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
             const float inv = L > 0.f ? 1.f / L : 0.f;
             lds_u8 *stg = nb == 0 ? (lds_u8 *)slot0 : (lds_u8 *)slot1;
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
+            for (int mb = 0; mb < 4; ++mb) {
                 pin_acc(o[mb][nb]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int col = 256 * c + 32 * mb + 8 * i + 4 * hh;   // 4 columns, 8 bytes
+                    const int col = 128 * c + 32 * mb + 8 * i + 4 * hh;   // 4 columns, 8 bytes
                     v2i w2;
                     w2[0] = (int)pack_bf16(o[mb][nb][4 * i] * inv, o[mb][nb][4 * i + 1] * inv);
                     w2[1] = (int)pack_bf16(o[mb][nb][4 * i + 2] * inv, o[mb][nb][4 * i + 3] * inv);
@@ -447,8 +475,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
         for (int nb = 0; nb < 2; ++nb) {
             lds_u8 *stg = nb == 0 ? (lds_u8 *)slot0 : (lds_u8 *)slot1;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int hl = (tid >> 6) + 4 * k;   // head 32nb + hl
+            for (int k = 0; k < 32 / WAVES; ++k) {
+                const int hl = (tid >> 6) + WAVES * k;   // head 32nb + hl
                 const v4i v = lds_read_b128(stg + 1024 * hl + 16 * (u ^ hl));
                 *reinterpret_cast<v4i *>(dst + (size_t)(32 * nb + hl) * DV * 2 + 16 * u) = v;
             }
