@@ -41,6 +41,7 @@
 // waves stall on each other's compactions far less often.  At the end the
 // exact selection leaves min(k, p+1) entries, already in ascending order.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -460,18 +461,20 @@ __device__ int filter4(uint32_t *bk, IdxT *bi, int cnt, uint32_t gt_than, uint32
 template <typename IdxT>
 __device__ int filter_gt(uint32_t *bk, IdxT *bi, int cnt, uint32_t gt, uint32_t *pad_k, IdxT *pad_i, int lane) {
     int out = 0;
-    uint32_t k[4];
-    IdxT ix[4];
-    if (cnt > 0) load4(bk, bi, 4 * lane, k, ix);
-    for (int base = 0; base < cnt; base += kStep) {
+    // two register buffers by step parity, so that the next step's entries
+    // are read a whole step ahead without register moves (a move of a
+    // register whose load is in flight would wait for it)
+    uint32_t k[2][4];
+    IdxT ix[2][4];
+    if (cnt > 0) load4(bk, bi, 4 * lane, k[0], ix[0]);
+    auto step = [&](auto P_, int base) {
+        constexpr int P = decltype(P_)::value;
         const int e0 = base + 4 * lane;
-        uint32_t kn[4];
-        IdxT ixn[4];
-        if (base + kStep < cnt) load4(bk, bi, e0 + kStep, kn, ixn);
-        const uint64_t K0 = ballot(e0 < cnt && k[0] > gt);
-        const uint64_t K1 = ballot(e0 + 1 < cnt && k[1] > gt);
-        const uint64_t K2 = ballot(e0 + 2 < cnt && k[2] > gt);
-        const uint64_t K3 = ballot(e0 + 3 < cnt && k[3] > gt);
+        if (base + kStep < cnt) load4(bk, bi, e0 + kStep, k[P ^ 1], ix[P ^ 1]);
+        const uint64_t K0 = ballot(e0 < cnt && k[P][0] > gt);
+        const uint64_t K1 = ballot(e0 + 1 < cnt && k[P][1] > gt);
+        const uint64_t K2 = ballot(e0 + 2 < cnt && k[P][2] > gt);
+        const uint64_t K3 = ballot(e0 + 3 < cnt && k[P][3] > gt);
         const int kp0 = (int)((K0 >> lane) & 1u), kp1 = (int)((K1 >> lane) & 1u);
         const int kp2 = (int)((K2 >> lane) & 1u), kp3 = (int)((K3 >> lane) & 1u);
         const int p0 = out + lanes_below(K0) + lanes_below(K1) + lanes_below(K2) + lanes_below(K3);
@@ -485,12 +488,14 @@ __device__ int filter_gt(uint32_t *bk, IdxT *bi, int cnt, uint32_t gt, uint32_t 
         IdxT *c2 = kp2 ? bi + p2 : pad_i + lane;
         IdxT *c3 = kp3 ? bi + p3 : pad_i + lane;
         wave_lds_order();
-        *a0 = k[0]; *a1 = k[1]; *a2 = k[2]; *a3 = k[3];
-        *c0 = ix[0]; *c1 = ix[1]; *c2 = ix[2]; *c3 = ix[3];
+        *a0 = k[P][0]; *a1 = k[P][1]; *a2 = k[P][2]; *a3 = k[P][3];
+        *c0 = ix[P][0]; *c1 = ix[P][1]; *c2 = ix[P][2]; *c3 = ix[P][3];
         wave_lds_order();
         out += __popcll(K0) + __popcll(K1) + __popcll(K2) + __popcll(K3);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { k[j] = kn[j]; ix[j] = ixn[j]; }
+    };
+    for (int base = 0; base < cnt; base += 2 * kStep) {
+        step(std::integral_constant<int, 0>{}, base);
+        if (base + kStep < cnt) step(std::integral_constant<int, 1>{}, base + kStep);
     }
     return out;
 }
@@ -591,11 +596,20 @@ __device__ void rebuild_hist(const uint32_t *bkey, BinState &st, uint32_t lo, ui
     st.lo = lo;
     for (int j = lane; j < kHistWords; j += kWave) hist[j] = 0;
     wave_lds_order();
-    for (int base = 0; base < st.cnt; base += kStep) {
+    // the next step's keys are read before this step's counts are added (two
+    // register buffers by step parity; the buffer is padded for the overread)
+    v4u kk[2];
+    if (st.cnt > 0) kk[0] = *reinterpret_cast<const v4u *>(bkey + 4 * lane);
+    auto step = [&](auto P_, int base) {
+        constexpr int P = decltype(P_)::value;
         const int e0 = base + 4 * lane;
-        const v4u kk = *reinterpret_cast<const v4u *>(bkey + e0);
+        if (base + kStep < st.cnt) kk[P ^ 1] = *reinterpret_cast<const v4u *>(bkey + e0 + kStep);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) atomicAdd(&hist[e0 + j < st.cnt ? bin_of(kk[j], lo) : 256u + lane], 1u);
+        for (int j = 0; j < 4; ++j) atomicAdd(&hist[e0 + j < st.cnt ? bin_of(kk[P][j], lo) : 256u + lane], 1u);
+    };
+    for (int base = 0; base < st.cnt; base += 2 * kStep) {
+        step(std::integral_constant<int, 0>{}, base);
+        if (base + kStep < st.cnt) step(std::integral_constant<int, 1>{}, base + kStep);
     }
     wave_lds_order();
     st.binned = true;
