@@ -596,20 +596,11 @@ __device__ void rebuild_hist(const uint32_t *bkey, BinState &st, uint32_t lo, ui
     st.lo = lo;
     for (int j = lane; j < kHistWords; j += kWave) hist[j] = 0;
     wave_lds_order();
-    // the next step's keys are read before this step's counts are added (two
-    // register buffers by step parity; the buffer is padded for the overread)
-    v4u kk[2];
-    if (st.cnt > 0) kk[0] = *reinterpret_cast<const v4u *>(bkey + 4 * lane);
-    auto step = [&](auto P_, int base) {
-        constexpr int P = decltype(P_)::value;
+    for (int base = 0; base < st.cnt; base += kStep) {
         const int e0 = base + 4 * lane;
-        if (base + kStep < st.cnt) kk[P ^ 1] = *reinterpret_cast<const v4u *>(bkey + e0 + kStep);
+        const v4u kk = *reinterpret_cast<const v4u *>(bkey + e0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) atomicAdd(&hist[e0 + j < st.cnt ? bin_of(kk[P][j], lo) : 256u + lane], 1u);
-    };
-    for (int base = 0; base < st.cnt; base += 2 * kStep) {
-        step(std::integral_constant<int, 0>{}, base);
-        if (base + kStep < st.cnt) step(std::integral_constant<int, 1>{}, base + kStep);
+        for (int j = 0; j < 4; ++j) atomicAdd(&hist[e0 + j < st.cnt ? bin_of(kk[j], lo) : 256u + lane], 1u);
     }
     wave_lds_order();
     st.binned = true;
