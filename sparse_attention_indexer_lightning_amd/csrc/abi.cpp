@@ -99,6 +99,18 @@ idxc_status check_indexer_call(const idxc_indexer_desc *d, const void *q, const 
     return IDXC_OK;
 }
 
+// When the row top-k takes its split path over exactly the score kernel's key
+// ranges, the score kernel writes the per-split bounds itself (one pass over
+// the scores fewer).  Sets a.split_bound and returns whether it did.
+int fuse_split_bounds(idxc::IndexerArgs &a, const idxc::TopkArgs &ta) {
+    int S, N, ns, sp;
+    if (!idxc::row_topk_split_geometry(ta.R, ta.Lk, &S, &N)) return 0;
+    idxc::decode_split_geometry(a, &ns, &sp);
+    if (ns != S || sp != N) return 0;
+    a.split_bound = idxc::row_topk_split_bounds(ta.ws, ta.R, ta.Lk);
+    return 1;
+}
+
 idxc_status run_indexer(const idxc_indexer_desc *d, const void *q, const void *k, const void *w, int32_t *t,
                         float *scores_dbg, void *ws, Path path, hipStream_t stream) {
     if (path == Path::Fused) {
@@ -107,8 +119,6 @@ idxc_status run_indexer(const idxc_indexer_desc *d, const void *q, const void *k
     }
     float *scores = static_cast<float *>(ws);
     idxc::IndexerArgs a = make_args(d, q, k, w, t, scores);
-    hipError_t e = idxc::launch_indexer_scores(a, stream);
-    if (e != hipSuccess) return IDXC_ERR_HIP;
     idxc::TopkArgs ta;
     ta.scores = scores;
     ta.row_pos = nullptr;
@@ -119,6 +129,9 @@ idxc_status run_indexer(const idxc_indexer_desc *d, const void *q, const void *k
     ta.t_out = t;
     ta.ws = static_cast<unsigned char *>(ws) + decode_scores_bytes(d);
     ta.ws_bytes = idxc::row_topk_ws_bytes(ta.R, ta.Lk);
+    ta.bounds_given = fuse_split_bounds(a, ta);
+    hipError_t e = idxc::launch_indexer_scores(a, stream);
+    if (e != hipSuccess) return IDXC_ERR_HIP;
     e = idxc::launch_row_topk(ta, stream);
     if (e != hipSuccess) return IDXC_ERR_HIP;
     if (scores_dbg)
@@ -260,8 +273,6 @@ idxc_status run_indexer_paged(const idxc_paged_indexer_desc *d, const void *q, c
     pk.bs_log2 = log2i(d->block_size);
     pk.max_blocks = d->max_blocks;
     pk.num_blocks = d->num_blocks;
-    e = idxc::launch_indexer_scores(a, stream, &pk);
-    if (e != hipSuccess) return IDXC_ERR_HIP;
     idxc::TopkArgs ta;
     ta.scores = scores;
     ta.row_pos = pos;
@@ -272,6 +283,9 @@ idxc_status run_indexer_paged(const idxc_paged_indexer_desc *d, const void *q, c
     ta.t_out = t;
     ta.ws = wsb + lay.topk;
     ta.ws_bytes = lay.total - lay.topk;
+    ta.bounds_given = fuse_split_bounds(a, ta);
+    e = idxc::launch_indexer_scores(a, stream, &pk);
+    if (e != hipSuccess) return IDXC_ERR_HIP;
     return from_hip(idxc::launch_row_topk(ta, stream));
 }
 

@@ -45,6 +45,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "select_common.h"
 
 namespace idxc {
 namespace {
@@ -1149,6 +1150,9 @@ struct ScoreParams {
     const int32_t *block_table;
     const int2 *row_info;
     int bs_log2, max_blocks, num_blocks;
+    // optional: each key range's top-k bound, bound[row][range] (split_bound)
+    uint32_t *bound;
+    int topk;
 };
 
 constexpr int kDecodeWaves = 4;
@@ -1161,6 +1165,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_p
 void decode_scores_kernel(ScoreParams p) {
     using S = Shape<E, D>;
     constexpr int H = 64;
+    __shared__ BoundShared bsh;
+    uint32_t top[kLocal] = {0u, 0u, 0u, 0u};   // this thread's 4 largest keys (bound)
     const int tid = threadIdx.x, lane = tid % kWave, g = lane >> 4, n = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int row = blockIdx.y;
@@ -1176,6 +1182,12 @@ void decode_scores_kernel(ScoreParams p) {
     const int s0 = blockIdx.x * p.split;
     const int s1 = min(s0 + p.split, p.Lk);
     float *out = p.scores + (size_t)row * p.Lk;
+    // the key range's bound from every thread's top keys (whole block)
+    auto write_bound = [&]() {
+        if (!p.bound) return;
+        const uint32_t bd = split_bound<kDecodeWaves * kWave>(bsh, top, pos + 1, p.split, (int)blockIdx.x, p.topk);
+        if (threadIdx.x == 0) p.bound[(size_t)blockIdx.y * gridDim.x + blockIdx.x] = bd;
+    };
 
     constexpr bool kMfma32 = E == Enc::FP8 && D == 128;
     Frag<E, D> A[4];
@@ -1240,6 +1252,7 @@ void decode_scores_kernel(ScoreParams p) {
             const float sc = score64_mfma32_b(Q32f, B);
             const int s = base + lane;
             if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
+            if (s < s1 && s <= pos) keep_top4(top, score_key(sc));
         };
         const int last = min(s1, pos + 1);        // keys at or before the query position
         int base = s0 + wave * KB;
@@ -1265,6 +1278,7 @@ void decode_scores_kernel(ScoreParams p) {
             const int s = base + lane;
             if (s < s1) out[s] = -INFINITY;
         }
+        write_bound();
         return;
     }
     for (int base = s0 + wave * KB; base < s1; base += kDecodeWaves * KB) {
@@ -1299,7 +1313,9 @@ void decode_scores_kernel(ScoreParams p) {
         }
         const float sc = transpose_reduce4(part[0], part[1], part[2], part[3]);
         if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
+        if (s < s1 && s <= pos) keep_top4(top, score_key(sc));
     }
+    write_bound();
 }
 
 template <Enc E, int D, int H, typename IdxT>
@@ -1403,11 +1419,10 @@ hipError_t launch_decode_d(const IndexerArgs &a, hipStream_t st, const PagedKeys
     // one round of workgroups: two per compute unit (the kernel's register
     // use allows two resident), each a contiguous key range of a multiple of
     // 256 keys (one 64-key block per wavefront and iteration)
-    const int rows = a.B * a.Lq;
-    const int max_split = (a.Lk + 255) / 256;
-    const int want = std::max(1, std::min(max_split, (2 * kComputeUnits + rows - 1) / rows));
-    p.split = ((a.Lk + want - 1) / want + 255) / 256 * 256;
-    const int nsplit = (a.Lk + p.split - 1) / p.split;
+    int nsplit;
+    decode_split_geometry(a, &nsplit, &p.split);
+    p.bound = a.split_bound;
+    p.topk = a.topk;
     if (pk) {
         p.block_table = pk->block_table;
         p.row_info = reinterpret_cast<const int2 *>(pk->row_info);
@@ -1439,6 +1454,14 @@ hipError_t launch_indexer_prefill(const IndexerArgs &a, hipStream_t st) {
         if (a.D == 128) return launch_prefill_d<Enc::BF16, 128>(a, st);
     }
     return hipErrorInvalidValue;
+}
+
+void decode_split_geometry(const IndexerArgs &a, int *nsplit, int *split) {
+    const int rows = a.B * a.Lq;
+    const int max_split = (a.Lk + 255) / 256;
+    const int want = std::max(1, std::min(max_split, (2 * kComputeUnits + rows - 1) / rows));
+    *split = ((a.Lk + want - 1) / want + 255) / 256 * 256;
+    *nsplit = (a.Lk + *split - 1) / *split;
 }
 
 bool decode_supported(const IndexerArgs &a) {

@@ -14,6 +14,9 @@ struct IndexerArgs {
     float *scores;   // prefill: optional debug copy; decode: required score rows
     int B, Lq, Lk, H, D, topk;
     Enc qk_enc, w_enc;
+    // decode: when set, the score kernel also writes every key range's top-k
+    // bound here ([rows][ranges], as the row top-k's split bounds)
+    uint32_t *split_bound = nullptr;
 };
 
 // Fused score + streaming top-k for prefill-shaped problems.  Returns
@@ -36,6 +39,8 @@ struct PagedKeys {
 // Scores of every (query, key <= position) into a.scores [B*Lq, Lk], keys
 // split over many workgroups; -inf beyond each query's position.
 bool decode_supported(const IndexerArgs &a);
+// Key ranges of the decode score kernel: nsplit ranges of `split` keys per row.
+void decode_split_geometry(const IndexerArgs &a, int *nsplit, int *split);
 hipError_t launch_indexer_scores(const IndexerArgs &a, hipStream_t s, const PagedKeys *paged = nullptr);
 
 // Serving metadata: row_info[r] = (sequence, position) of query row r from
@@ -65,8 +70,13 @@ struct TopkArgs {
     int32_t *t_out;
     void *ws;         // device workspace of ws_bytes bytes (16-byte aligned), may be NULL if not needed
     size_t ws_bytes;
+    int bounds_given = 0;   // split path: the per-split bounds in ws were written by the score kernel
 };
 size_t row_topk_ws_bytes(int R, int Lk);
+// The split path's geometry (S splits of N keys per row; false: one workgroup
+// per row) and the address of its per-split bounds [R][S] in a workspace.
+bool row_topk_split_geometry(int R, int Lk, int *S, int *N);
+uint32_t *row_topk_split_bounds(void *ws, int R, int Lk);
 hipError_t launch_row_topk(const TopkArgs &a, hipStream_t s);
 
 // counts[r] = |{t_a[r][j] >= 0} intersected with {t_b[r][j] >= 0}|; rows

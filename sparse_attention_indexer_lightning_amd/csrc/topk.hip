@@ -32,17 +32,15 @@
 // not fit in LDS, the row falls back to radix selection over the row in HBM.
 #include "device_common.h"
 #include "kernels.h"
+#include "select_common.h"
 
 namespace idxc {
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kLocal = 4;                  // keys kept per thread in step 1
 constexpr int kUnion = kThreads * kLocal;  // 4096
 constexpr int kCandCap = 8192;             // LDS candidate capacity
-constexpr int kDigit = 11;                 // radix digit width
-constexpr int kBins = 1 << kDigit;
 
 struct TopkShared {
     uint32_t ukey[kUnion];          // step 1 union, then reused
@@ -53,92 +51,6 @@ struct TopkShared {
     int sh_bin;
     uint32_t sh_above;
 };
-
-__device__ __forceinline__ uint32_t wave_max32(uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-    return v;
-}
-
-// Insert u into a descending list of the 4 largest keys seen.
-__device__ __forceinline__ void keep_top4(uint32_t (&top)[kLocal], uint32_t u) {
-    if (u > top[3]) {
-        top[3] = u;
-        if (top[3] > top[2]) { const uint32_t x = top[2]; top[2] = top[3]; top[3] = x; }
-        if (top[2] > top[1]) { const uint32_t x = top[1]; top[1] = top[2]; top[2] = x; }
-        if (top[1] > top[0]) { const uint32_t x = top[0]; top[0] = top[1]; top[1] = x; }
-    }
-}
-
-// The need-th largest key among `n` keys produced by get(i) (block-wide),
-// returning the key and, through *above, how many keys are strictly larger.
-// MSB-first radix select with 11-bit digits, starting below the bits that the
-// smallest and largest key share (so the first digit already spreads keys).
-template <int NT = kThreads, typename Sh, typename Get>
-__device__ uint32_t block_select(Sh &sh, int n, int need, Get get, uint32_t *above_out) {
-    constexpr int NW = NT / kWave;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int i = tid; i < n; i += NT) {
-        const uint32_t u = get(i);
-        mn = min(mn, u);
-        mx = max(mx, u);
-    }
-    mn = ~wave_max32(~mn);
-    mx = wave_max32(mx);
-    if (lane == 0) { sh.wtot[0][wave] = mn; sh.wtot[1][wave] = mx; }
-    __syncthreads();
-    mn = 0xFFFFFFFFu; mx = 0u;
-    for (int w = 0; w < NW; ++w) { mn = min(mn, sh.wtot[0][w]); mx = max(mx, sh.wtot[1][w]); }
-    int top = (mn == mx) ? 0 : 32 - __builtin_clz(mn ^ mx);
-    uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
-    uint32_t prefix = mn & pmask;
-    uint32_t above_total = 0;
-    while (top > 0) {
-        const int width = top < kDigit ? top : kDigit;
-        const int shift = top - width;
-        const uint32_t dmask = (1u << width) - 1u;
-        for (int j = tid; j < kBins; j += NT) sh.hist[j] = 0;
-        __syncthreads();
-        for (int i = tid; i < n; i += NT) {
-            const uint32_t u = get(i);
-            if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & dmask], 1u);
-        }
-        __syncthreads();
-        // suffix scan over kBins bins: lane l of wave 0 owns bins [32l, 32l+32)
-        if (wave == 0) {
-            uint32_t sum = 0;
-            for (int j = 0; j < kBins / kWave; ++j) sum += sh.hist[(kBins / kWave) * lane + j];
-            uint32_t S = sum;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t v = __shfl_down(S, o, kWave);
-                if (lane + o < kWave) S += v;
-            }
-            const uint32_t E = S - sum;
-            if (E < (uint32_t)need && S >= (uint32_t)need) {
-                uint32_t c = E;
-                int bsel = 0;
-                for (int j = kBins / kWave - 1; j >= 0; --j) {
-                    const uint32_t h = sh.hist[(kBins / kWave) * lane + j];
-                    if (c + h >= (uint32_t)need) { bsel = j; break; }
-                    c += h;
-                }
-                sh.sh_bin = (kBins / kWave) * lane + bsel;
-                sh.sh_above = c;
-            }
-        }
-        __syncthreads();
-        prefix |= (uint32_t)sh.sh_bin << shift;
-        pmask |= dmask << shift;
-        need -= (int)sh.sh_above;
-        above_total += sh.sh_above;
-        top = shift;
-        __syncthreads();
-    }
-    *above_out = above_total;
-    return prefix;
-}
 
 // Ordered output of the top-k from keys get(i), i < n, in index order:
 // slot = above_before + min(equal_before, need_eq), index = idx(i).
@@ -204,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void row_topk_kernel(TopkArgs a) {
     for (int i = 0; i < kLocal; ++i) sh.ukey[tid * kLocal + i] = top[i];
     __syncthreads();
     uint32_t dummy;
-    const uint32_t bound = block_select(sh, kUnion, k, [&](int i) { return sh.ukey[i]; }, &dummy);
+    const uint32_t bound = block_select<kThreads>(sh, kUnion, k, [&](int i) { return sh.ukey[i]; }, &dummy);
 
     // 2. collect keys >= bound in index order (4 per thread per step)
     uint32_t base = 0;
@@ -250,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void row_topk_kernel(TopkArgs a) {
         // 3. exact selection among the candidates
         const int nc = (int)base;
         uint32_t above;
-        const uint32_t theta = block_select(sh, nc, k, [&](int i) { return sh.ckey[i]; }, &above);
+        const uint32_t theta = block_select<kThreads>(sh, nc, k, [&](int i) { return sh.ckey[i]; }, &above);
         const int need_eq = k - (int)above;
         ordered_output(sh, nc, theta, need_eq, k, [&](int i) { return sh.ckey[i]; },
                        [&](int i) { return sh.cidx[i]; }, out);
@@ -258,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void row_topk_kernel(TopkArgs a) {
     }
     // fallback: radix selection over the row in HBM
     uint32_t above;
-    const uint32_t theta = block_select(sh, n, k, [&](int i) { return score_key(s[i]); }, &above);
+    const uint32_t theta = block_select<kThreads>(sh, n, k, [&](int i) { return score_key(s[i]); }, &above);
     ordered_output(sh, n, theta, k - (int)above, k, [&](int i) { return score_key(s[i]); },
                    [&](int i) { return i; }, out);
 }
@@ -271,13 +183,6 @@ constexpr int kMinSplit = 4096;        // keys per split at least
 constexpr int kSplitTarget = 512;      // aim for about this many workgroups in total
 constexpr int kSplitVec = 16;          // keys per thread per step (loads in flight)
 
-struct SplitShared {
-    uint32_t ukey[kSplitThreads * kLocal];
-    uint32_t hist[kBins];
-    uint32_t wtot[2][kSplitWaves];
-    int sh_bin;
-    uint32_t sh_above;
-};
 
 struct SplitPlan {
     int S;          // splits per row (1: whole-row kernel)
@@ -291,7 +196,7 @@ __host__ inline SplitPlan split_plan(int R, int Lk) {
     if (S > Lk / kMinSplit) S = Lk / kMinSplit;
     if (S < 2) return pl;
     pl.S = S;
-    pl.N = (Lk + S - 1) / S;
+    pl.N = ((Lk + S - 1) / S + 255) / 256 * 256;   // whole 256-key steps, as the decode score kernel's ranges
     return pl;
 }
 
@@ -325,45 +230,30 @@ __device__ __forceinline__ int row_valid(const TopkArgs &a, int r) {
     return pos + 1 > 0 ? pos + 1 : 0;
 }
 
-// 1. per split: a lower bound on its m-th largest key.  Only the F = n / N
-// completely filled splits of a row vouch for keys, m = ceil(k / F) each;
-// the others report the neutral maximum.  With F = 0, or m beyond the
-// per-thread lists, the bound is 0 (no pruning for the row).
+// 1. per split: a lower bound on its m-th largest key (split_bound).  The
+// decode score kernel computes the same bounds while scoring when its key
+// ranges are these splits; the launch then skips this kernel.
 __global__ __launch_bounds__(kSplitThreads) void topk_split_bound(TopkArgs a, SplitPlan pl, SplitWs ws) {
-    __shared__ SplitShared sh;
+    __shared__ BoundShared sh;
     const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const int n = row_valid(a, r);
-    const int full = n / pl.N;
-    uint32_t *dst = ws.bound + (size_t)r * pl.S + s;
-    if (full == 0 || s >= full) {
-        if (tid == 0) *dst = (full == 0 && s == 0) ? 0u : 0xFFFFFFFFu;
-        return;
-    }
-    const int m = (a.topk + full - 1) / full;
-    if (m > kSplitThreads * kLocal) {
-        if (tid == 0) *dst = 0u;
-        return;
-    }
-    const int j0 = s * pl.N, j1 = j0 + pl.N;
+    const int j0 = s * pl.N, j1 = min(j0 + pl.N, n);
     const float *row = a.scores + (size_t)r * a.Lk;
     uint32_t top[kLocal] = {0u, 0u, 0u, 0u};
-    for (int c0 = j0; c0 < j1; c0 += kSplitVec * kSplitThreads) {
-        float v[kSplitVec];
+    if (n / pl.N > s) {   // filled splits only (split_bound ignores the others)
+        for (int c0 = j0; c0 < j1; c0 += kSplitVec * kSplitThreads) {
+            float v[kSplitVec];
 #pragma unroll
-        for (int e = 0; e < kSplitVec; ++e) {
-            const int j = c0 + e * kSplitThreads + tid;
-            v[e] = j < j1 ? row[j] : -INFINITY;
+            for (int e = 0; e < kSplitVec; ++e) {
+                const int j = c0 + e * kSplitThreads + tid;
+                v[e] = j < j1 ? row[j] : -INFINITY;
+            }
+#pragma unroll
+            for (int e = 0; e < kSplitVec; ++e) keep_top4(top, score_key(v[e]));
         }
-#pragma unroll
-        for (int e = 0; e < kSplitVec; ++e) keep_top4(top, score_key(v[e]));
     }
-#pragma unroll
-    for (int i = 0; i < kLocal; ++i) sh.ukey[tid * kLocal + i] = top[i];
-    __syncthreads();
-    uint32_t dummy;
-    const uint32_t b = block_select<kSplitThreads>(sh, kSplitThreads * kLocal, m, [&](int i) { return sh.ukey[i]; },
-                                                   &dummy);
-    if (tid == 0) *dst = b;
+    const uint32_t b = split_bound<kSplitThreads>(sh, top, n, pl.N, s, a.topk);
+    if (tid == 0) ws.bound[(size_t)r * pl.S + s] = b;
 }
 
 // 2. per split: keys >= theta = min over the row's bounds, in index order.
@@ -447,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_select(TopkArgs a, SplitP
         }
         __syncthreads();
         uint32_t above;
-        const uint32_t theta = block_select(sh, total, k, [&](int i) { return sh.ckey[i]; }, &above);
+        const uint32_t theta = block_select<kThreads>(sh, total, k, [&](int i) { return sh.ckey[i]; }, &above);
         ordered_output(sh, total, theta, k - (int)above, k, [&](int i) { return sh.ckey[i]; },
                        [&](int i) { return sh.cidx[i]; }, out);
         return;
@@ -455,12 +345,24 @@ __global__ __launch_bounds__(kThreads) void topk_split_select(TopkArgs a, SplitP
     // too many candidates for LDS: radix selection over the row in HBM
     const float *srow = a.scores + (size_t)r * a.Lk;
     uint32_t above;
-    const uint32_t theta = block_select(sh, n, k, [&](int i) { return score_key(srow[i]); }, &above);
+    const uint32_t theta = block_select<kThreads>(sh, n, k, [&](int i) { return score_key(srow[i]); }, &above);
     ordered_output(sh, n, theta, k - (int)above, k, [&](int i) { return score_key(srow[i]); },
                    [&](int i) { return i; }, out);
 }
 
 }  // namespace
+
+bool row_topk_split_geometry(int R, int Lk, int *S, int *N) {
+    const SplitPlan pl = split_plan(R, Lk);
+    *S = pl.S;
+    *N = pl.N;
+    return pl.S > 1;
+}
+
+uint32_t *row_topk_split_bounds(void *ws, int R, int Lk) {
+    const SplitPlan pl = split_plan(R, Lk);
+    return pl.S > 1 ? split_ws(ws, R, pl).bound : nullptr;
+}
 
 size_t row_topk_ws_bytes(int R, int Lk) {
     const SplitPlan pl = split_plan(R, Lk);
@@ -479,7 +381,7 @@ hipError_t launch_row_topk(const TopkArgs &a, hipStream_t st) {
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         const dim3 g((unsigned)pl.S, (unsigned)a.R);
-        hipLaunchKernelGGL(topk_split_bound, g, dim3(kSplitThreads), 0, st, a, pl, ws);
+        if (!a.bounds_given) hipLaunchKernelGGL(topk_split_bound, g, dim3(kSplitThreads), 0, st, a, pl, ws);
         hipLaunchKernelGGL(topk_split_collect, g, dim3(kSplitThreads), 0, st, a, pl, ws);
         hipLaunchKernelGGL(topk_split_select, dim3((unsigned)a.R), dim3(kThreads), lds, st, a, pl, ws);
         return hipGetLastError();
