@@ -55,6 +55,15 @@ constexpr int kMaxThreads = 512;
 constexpr int kChunkMax = 4;    // 16-byte chunks each thread stages per key block
 constexpr int kPadEntries = 256; // candidate-buffer padding read by 4-per-lane passes
 constexpr int kHistWords = 320;  // 256 bins + one dummy slot per lane for masked-off updates
+// Sampled starting threshold of the 64-head sweep: every kSampleStride-th key
+// block is scored first; a row's threshold is then its sample's r-th largest
+// key, r = kSampleMargin * k * (sampled keys) / (keys), unless r is below
+// kSampleMinRank or above the sample.  Only workgroups with at least
+// kSampleMinBlocks key blocks sample.
+constexpr int kSampleStride = 32;
+constexpr int kSampleMargin = 2;
+constexpr int kSampleMinRank = 32;
+constexpr int kSampleMinBlocks = 64;
 
 template <Enc E, int D>
 struct Shape {
@@ -105,9 +114,14 @@ __device__ __forceinline__ v4f frag_mma(const Frag<E, D> &a, const Frag<E, D> &b
     return acc;
 }
 
+// One 32-bit load whatever the encoding, chosen by selects rather than a
+// branch, so that a run of weight loads stays in flight together (a branch
+// per load ends each one with a full wait).  bf16: the word holding entry
+// idx; rows hold an even number of heads, so the word lies inside the row.
 __device__ __forceinline__ float load_w(const void *w, Enc enc, size_t idx) {
-    if (enc == Enc::BF16) return bf16_to_f32(reinterpret_cast<const uint16_t *>(w)[idx]);
-    return reinterpret_cast<const float *>(w)[idx];
+    const bool h16 = enc == Enc::BF16;
+    const uint32_t word = reinterpret_cast<const uint32_t *>(w)[h16 ? idx >> 1 : idx];
+    return __uint_as_float(!h16 ? word : (idx & 1) ? (word & 0xFFFF0000u) : (word << 16));
 }
 
 // Lane group g (lanes 16g..16g+15) holds partial sums p[j] of sub-block j for
@@ -780,7 +794,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         rcnt[wave * TW + t] = 0;
         rthr[wave * TW + t] = 0u;
     }
-    if (tid < 3) flags[tid] = 0;
+    if (tid < 4) flags[tid] = 0;   // words 0-2: compaction requests; word 3: the sample failed
     BinState st;
     st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u; st.binned = false;
     const int want_level = p.topk + (p.cap - p.topk) / 2;
@@ -902,24 +916,62 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         auto stash1 = [&](int buf, const v4i &v) {
             *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + krow * S::PITCH + kcol) = v;
         };
-        v4i kr[2];
-        kr[0] = fetch1(0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // queries, weights and block 0
-        stash1(0, kr[0]);
-        kr[1] = fetch1(1);
-        lds_barrier();
-
-        const v16f z = {};
-        v16f a1[2] = {z, z};   // key fragment 1 of the previous block
-        float p0_prev = 0.f;   // epilogue of key fragment 0 of the previous block
         auto combine = [](float p0, float p1) {
             // lanes 0-31 hold key fragment 0 of their head half, lanes 32-63 the other half
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
             return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         };
+        // Sampled start.  The sweep first visits the ns sampled blocks 0, 32,
+        // 64, ... and then every block in order (iteration it -> block
+        // bmap(it)).  After the sample's selection each row keeps only its
+        // threshold tau, the r-th largest sampled key, and empties its buffer;
+        // the full sweep then appends the keys above tau (the sampled blocks
+        // again, so the buffer stays in index order).  If the row ends with
+        // at least k entries, its k-th largest key is above tau and every
+        // key that tau filtered out lies below it: the result is exact.  A
+        // row left with fewer than k entries makes its workgroup sweep again
+        // without the sample.  For i.i.d. scores r is about 2k/32 = 128 and a
+        // shortfall is a many-sigma event; a row then appends about 2k keys
+        // instead of k(1 + ln(n/k)), and compacts a few times instead of ~16.
+        int ns = nblk >= kSampleMinBlocks ? (nblk - 1) / kSampleStride + 1 : 0;
+        auto bmap = [&](int it) { return it < ns ? it * kSampleStride : it - ns; };
+        auto tau_step = [&]() {
+            const int i = i0 + wave;
+            if (i >= p.Lq) return;
+            const int pos = off + i;
+            int nsk = 0;   // sampled keys at or before the row's position
+            for (int j = 0; j < ns; ++j) {
+                const int lo = j * kSampleStride * KB;
+                if (lo <= pos) nsk += min(KB, pos + 1 - lo);
+            }
+            const int r = (int)(((long long)kSampleMargin * p.topk * nsk + pos) / (pos + 1));
+            uint32_t thr = 0u;   // 0: no filter
+            if (r >= kSampleMinRank && r <= st.cnt) {
+                int c = st.cnt;
+                thr = select_compact<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, c, r, hist,
+                                           lane);
+            }
+            st.cnt = 0;
+            st.thr = thr;
+            st.thr_f = key_floor_float(thr);
+            st.lo = 0u;
+            st.binned = false;
+        };
+        for (;;) {
+        const int niter = ns + nblk;
+        v4i kr[2];
+        kr[0] = fetch1(bmap(0));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // queries, weights and the first block
+        stash1(0, kr[0]);
+        kr[1] = fetch1(bmap(1));
+        lds_barrier();
+
+        const v16f z = {};
+        v16f a1[2] = {z, z};   // key fragment 1 of the previous block
+        float p0_prev = 0.f;   // epilogue of key fragment 0 of the previous block
         auto iter = [&](auto PAR_, int blk) {
-            constexpr int PAR = decltype(PAR_)::value;   // == blk & 1
-            kr[PAR] = fetch1(blk + 2);
+            constexpr int PAR = decltype(PAR_)::value;   // == blk & 1 (blk: the iteration)
+            kr[PAR] = fetch1(bmap(blk + 2));
             const unsigned char *kt = ktile + (size_t)PAR * KB * S::PITCH;
             v8i B[2][2];
 #pragma unroll
@@ -947,7 +999,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             __builtin_amdgcn_sched_barrier(0);
             // block blk-1's selection (none before block 0: a base past every position)
             const float lin_prev = linbuf[(PAR ^ 1) * (8 * KB) + lin_get];
-            const bool need = select_binned(combine(p0_prev, p1) + lin_prev, blk >= 1 ? (blk - 1) * KB : INT_MAX);
+            const bool need = select_binned(combine(p0_prev, p1) + lin_prev, blk >= 1 ? bmap(blk - 1) * KB : INT_MAX);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rf = 0; rf < 2; ++rf) a1[rf] = mfma_fp8_32x32x64(Q32f.a[rf][0], B[1][0], z);
@@ -970,18 +1022,39 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             lds_barrier();
         };
         // unrolled by two: one copy of the body per register buffer of the staging loads
-        for (int blk = 0; blk < nblk; blk += 2) {
-            iter(std::integral_constant<int, 0>{}, blk);
-            compact_if_flagged(blk);
-            if (blk + 1 < nblk) {
-                iter(std::integral_constant<int, 1>{}, blk + 1);
-                compact_if_flagged(blk + 1);
+        for (int it = 0; it < niter; it += 2) {
+            iter(std::integral_constant<int, 0>{}, it);
+            compact_if_flagged(it);
+            if (ns > 0 && it == ns) tau_step();
+            if (it + 1 < niter) {
+                iter(std::integral_constant<int, 1>{}, it + 1);
+                compact_if_flagged(it + 1);
+                if (ns > 0 && it + 1 == ns) tau_step();
             }
         }
         // the last block's fragment 1 and its selection (room for it was made
         // by the last iteration's compactions)
-        (void)select_binned(combine(p0_prev, epi32_abs(a1[0], a1[1], Q32f)) + linbuf[((nblk - 1) & 1) * (8 * KB) + lin_get],
+        (void)select_binned(combine(p0_prev, epi32_abs(a1[0], a1[1], Q32f)) + linbuf[((niter - 1) & 1) * (8 * KB) + lin_get],
                             (nblk - 1) * KB);
+        if (ns == 0) break;
+        {
+            const int i = i0 + wave;
+            if (i < p.Lq && off + i + 1 > p.topk && st.cnt < p.topk && lane == 0) atomicOr(&flags[3], 1);
+        }
+        __syncthreads();
+        const bool again = flags[3] != 0;
+        __syncthreads();   // every wave has read the word
+        if (!again) break;
+        // sweep again without the sample, from empty buffers
+        if (tid < 4) flags[tid] = 0;
+        st.cnt = 0;
+        st.thr = 0u;
+        st.thr_f = -INFINITY;
+        st.lo = 0u;
+        st.binned = false;
+        ns = 0;
+        __syncthreads();
+        }
     } else {
     fetch(0);
     stash(0);
@@ -1217,12 +1290,12 @@ void decode_scores_kernel(ScoreParams p) {
         return p.k + (((size_t)pg << p.bs_log2) + (s & ((1 << p.bs_log2) - 1))) * S::ROWB;
     };
     if constexpr (kMfma32) {
-        // the keys of the next block are loaded while the current one is
-        // scored (two register buffers used in turn, so that no loaded value
-        // is moved before use): up to two blocks (16 KB) of loads in flight
-        // per wavefront.  The prefetch is unconditional, clamped to the last
-        // key, so that every iteration issues the same loads and the
-        // compiler's waits stay exact.
+        // the keys of the next two blocks are loaded while the current one is
+        // scored (three register buffers used in turn, so that no loaded value
+        // is moved before use): two blocks (16 KB) of loads stay in flight per
+        // wavefront through the scoring.  The prefetch is unconditional,
+        // clamped to the last key, so that every iteration issues the same
+        // loads and the compiler's waits stay exact.
         constexpr int STRIDE = kDecodeWaves * KB;
         // paged: a 64-key block lies in one page (pages hold a multiple of 64
         // keys); past the last valid key the last valid block is read again.
@@ -1256,23 +1329,28 @@ void decode_scores_kernel(ScoreParams p) {
         };
         const int last = min(s1, pos + 1);        // keys at or before the query position
         int base = s0 + wave * KB;
-        v8i B0[2][2], B1[2][2];
-        const unsigned char *pg1 = nullptr;
         if (base < last) {
+            v8i B0[2][2], B1[2][2], B2[2][2];
             load_block(B0, base, block_page(base));
-            pg1 = block_page(base + STRIDE);
-        }
-        for (; base < last; base += 2 * STRIDE) {
-            load_block(B1, base + STRIDE, pg1);
-            const unsigned char *pg2 = block_page(base + 2 * STRIDE);
-            score_block(B0, base);
-            if (base + STRIDE >= last) {
+            load_block(B1, base + STRIDE, block_page(base + STRIDE));
+            const unsigned char *pg = block_page(base + 2 * STRIDE);
+            for (;;) {
+                load_block(B2, base + 2 * STRIDE, pg);
+                pg = block_page(base + 3 * STRIDE);
+                score_block(B0, base);
                 base += STRIDE;
-                break;
+                if (base >= last) break;
+                load_block(B0, base + 2 * STRIDE, pg);
+                pg = block_page(base + 3 * STRIDE);
+                score_block(B1, base);
+                base += STRIDE;
+                if (base >= last) break;
+                load_block(B1, base + 2 * STRIDE, pg);
+                pg = block_page(base + 3 * STRIDE);
+                score_block(B2, base);
+                base += STRIDE;
+                if (base >= last) break;
             }
-            load_block(B0, base + 2 * STRIDE, pg2);
-            pg1 = block_page(base + 3 * STRIDE);
-            score_block(B1, base + STRIDE);
         }
         for (; base < s1; base += STRIDE) {
             const int s = base + lane;

@@ -181,7 +181,9 @@ constexpr int kSplitThreads = 256;
 constexpr int kSplitWaves = kSplitThreads / kWave;
 constexpr int kMinSplit = 4096;        // keys per split at least
 constexpr int kSplitTarget = 512;      // aim for about this many workgroups in total
-constexpr int kSplitVec = 16;          // keys per thread per step (loads in flight)
+constexpr int kSplitVec = 16;          // keys per thread per step
+constexpr int kCollectSteps = 4;       // collect: steps whose loads are issued together
+static_assert(kSplitTarget <= 8 * kWave, "split offsets: eight per lane of one wavefront");
 
 
 struct SplitPlan {
@@ -259,51 +261,61 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_bound(TopkArgs a, Sp
 // 2. per split: keys >= theta = min over the row's bounds, in index order.
 // Each step thread t looks at keys c0 + e * 256 + t (e < kSplitVec), so the
 // order is e-major; a per-(e, wave) count table gives every key its slot.
+// The loads of kCollectSteps steps are issued together and consumed in
+// order, so a split costs about one memory latency rather than one per step.
 __global__ __launch_bounds__(kSplitThreads) void topk_split_collect(TopkArgs a, SplitPlan pl, SplitWs ws) {
     __shared__ uint32_t wcnt[2][kSplitVec][kSplitWaves];
     const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int n = row_valid(a, r);
     const int j0 = s * pl.N, j1 = min(j0 + pl.N, n);
-    uint32_t theta = 0xFFFFFFFFu;
-    for (int i = 0; i < pl.S; ++i) theta = min(theta, ws.bound[(size_t)r * pl.S + i]);
+    uint32_t tmin = 0xFFFFFFFFu;   // theta: every lane loads some bounds, then a wave minimum
+    for (int i = lane; i < pl.S; i += kWave) tmin = min(tmin, ws.bound[(size_t)r * pl.S + i]);
+    const uint32_t theta = ~wave_max32(~tmin);
     const float *row = a.scores + (size_t)r * a.Lk;
     uint2 *out = ws.cand + ((size_t)r * pl.S + s) * pl.N;
+    constexpr int kChunk = kCollectSteps * kSplitVec * kSplitThreads;
     uint32_t base = 0;
     int par = 0;
-    for (int c0 = j0; c0 < j1; c0 += kSplitVec * kSplitThreads, par ^= 1) {
-        float v[kSplitVec];
+    for (int c1 = j0; c1 < j1; c1 += kChunk) {
+        float v[kCollectSteps * kSplitVec];
 #pragma unroll
-        for (int e = 0; e < kSplitVec; ++e) {
-            const int j = c0 + e * kSplitThreads + tid;
+        for (int e = 0; e < kCollectSteps * kSplitVec; ++e) {
+            const int j = c1 + e * kSplitThreads + tid;
             v[e] = j < j1 ? row[j] : -INFINITY;
         }
-        uint32_t u[kSplitVec];
-        uint64_t B[kSplitVec];
 #pragma unroll
-        for (int e = 0; e < kSplitVec; ++e) {
-            const int j = c0 + e * kSplitThreads + tid;
-            u[e] = score_key(v[e]);
-            B[e] = ballot(j < j1 && u[e] >= theta);
-            if (lane == 0) wcnt[par][e][wave] = (uint32_t)__popcll(B[e]);
-        }
-        __syncthreads();
-        uint32_t before = base;   // keys kept ahead of (e, wave) in this step
+        for (int q = 0; q < kCollectSteps; ++q) {
+            const int c0 = c1 + q * kSplitVec * kSplitThreads;
+            if (c0 >= j1) break;
+            uint32_t u[kSplitVec];
+            uint64_t B[kSplitVec];
 #pragma unroll
-        for (int e = 0; e < kSplitVec; ++e) {
-            uint32_t tot = 0, wb = 0;
-#pragma unroll
-            for (int w = 0; w < kSplitWaves; ++w) {
-                const uint32_t c = wcnt[par][e][w];
-                if (w < wave) wb += c;
-                tot += c;
-            }
-            if ((B[e] >> lane) & 1u) {
+            for (int e = 0; e < kSplitVec; ++e) {
                 const int j = c0 + e * kSplitThreads + tid;
-                out[before + wb + (uint32_t)lanes_below(B[e])] = make_uint2(u[e], (uint32_t)j);
+                u[e] = score_key(v[q * kSplitVec + e]);
+                B[e] = ballot(j < j1 && u[e] >= theta);
+                if (lane == 0) wcnt[par][e][wave] = (uint32_t)__popcll(B[e]);
             }
-            before += tot;
+            __syncthreads();
+            uint32_t before = base;   // keys kept ahead of (e, wave) in this step
+#pragma unroll
+            for (int e = 0; e < kSplitVec; ++e) {
+                uint32_t tot = 0, wb = 0;
+#pragma unroll
+                for (int w = 0; w < kSplitWaves; ++w) {
+                    const uint32_t c = wcnt[par][e][w];
+                    if (w < wave) wb += c;
+                    tot += c;
+                }
+                if ((B[e] >> lane) & 1u) {
+                    const int j = c0 + e * kSplitThreads + tid;
+                    out[before + wb + (uint32_t)lanes_below(B[e])] = make_uint2(u[e], (uint32_t)j);
+                }
+                before += tot;
+            }
+            base = before;
+            par ^= 1;
         }
-        base = before;
     }
     if (tid == 0) ws.count[(size_t)r * pl.S + s] = (int)base;
 }
@@ -320,20 +332,61 @@ __global__ __launch_bounds__(kThreads) void topk_split_select(TopkArgs a, SplitP
         for (int j = tid; j < k; j += kThreads) out[j] = j < n ? j : -1;
         return;
     }
-    int total = 0;
-    for (int i = 0; i < pl.S; ++i) total += ws.count[(size_t)r * pl.S + i];
+    // offsets of the splits' candidate lists (split order is index order):
+    // one wavefront loads every count at once, eight per lane, and scans them
+    int *soff = reinterpret_cast<int *>(sh.ukey);   // [S + 1]; ukey is unused here
+    const int S = pl.S;
+    if (tid < kWave) {
+        int c[8], sum = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 8 * tid + e;
+            c[e] = i < S ? ws.count[(size_t)r * S + i] : 0;
+            sum += c[e];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int t = __shfl_up(incl, d, kWave);
+            if (tid >= d) incl += t;
+        }
+        int run = incl - sum;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 8 * tid + e;
+            if (i < S) soff[i] = run;
+            run += c[e];
+        }
+        if (tid == kWave - 1) soff[S] = incl;
+    }
+    __syncthreads();
+    const int total = soff[S];
     if (total <= kCandCap) {
-        // gather the candidates of every split, in split order
-        int off = 0;
-        for (int i = 0; i < pl.S; ++i) {
-            const int c = ws.count[(size_t)r * pl.S + i];
-            const uint2 *src = ws.cand + ((size_t)r * pl.S + i) * pl.N;
-            for (int j = tid; j < c; j += kThreads) {
-                const uint2 v = src[j];
-                sh.ckey[off + j] = v.x;
-                sh.cidx[off + j] = (int32_t)v.y;
+        // gather the candidates of every split: candidate g of the row is
+        // entry g - soff[i] of the last split i with soff[i] <= g; each thread
+        // issues all its loads before storing any
+        constexpr int kPer = kCandCap / kThreads;
+        uint2 v[kPer];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int gi = tid + e * kThreads;
+            if (gi < total) {
+                int lo = 0, hi = S - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (soff[mid] <= gi) lo = mid;
+                    else hi = mid - 1;
+                }
+                v[e] = ws.cand[((size_t)r * S + lo) * pl.N + (gi - soff[lo])];
             }
-            off += c;
+        }
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int gi = tid + e * kThreads;
+            if (gi < total) {
+                sh.ckey[gi] = v[e].x;
+                sh.cidx[gi] = (int32_t)v[e].y;
+            }
         }
         __syncthreads();
         uint32_t above;

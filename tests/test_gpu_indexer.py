@@ -174,3 +174,28 @@ def test_fused_and_split_paths_agree():
     check_index_sets(t_fused[:, 36:].cpu().numpy().reshape(8, -1), t_split.cpu().numpy().reshape(8, -1), so, pos,
                      700, RTOL["fp8"], "fused vs split")
     del wl2
+
+
+def test_sampled_threshold_fallback():
+    """The 64-head fused sweep starts each long row from a threshold taken on
+    every 32nd key block.  Here the keys of those blocks get four times the
+    norm, so the sample's threshold lies above nearly every other score: the
+    rows end with fewer than k candidates and their workgroups sweep again
+    without the sample.  T must be the exact top-k of the kernel's own scores
+    and agree with the oracle."""
+    Lq, Lk, topk = 24, 12000, 2048
+    wl = inputs.Workload("s", 1, Lq, Lk, 64, 128, topk, "fp8", "bf16", 21)
+    q, k, w = inputs.indexer_inputs(wl, 0, DEV)
+    kf = k.float()
+    sampled = (torch.arange(Lk, device=DEV) // 64) % 32 == 0
+    kf[:, sampled] = (kf[:, sampled] * 4).clamp(-448, 448)
+    k = kf.to(torch.float8_e4m3fn).contiguous()
+    t, scores = run_full(q, k, w, topk)
+    pos = oracle.row_positions(1, Lq, Lk)
+    sg = scores.cpu().numpy().reshape(Lq, Lk)
+    tg = t.cpu().numpy().reshape(Lq, topk)
+    assert np.array_equal(tg, oracle.topk(sg, pos, topk))
+    rows = np.array([0, 11, 23], dtype=np.int64)
+    to, so = indexer_oracle(q, k, w, topk, rows=rows)
+    check_scores(sg[rows], so, RTOL["fp8"], "sampled fallback")
+    check_index_sets(tg[rows], to, so, pos[rows], topk, RTOL["fp8"], "sampled fallback")

@@ -51,7 +51,7 @@ def test_all_equal_rows():
         assert np.array_equal(t, np.tile(np.arange(2048, dtype=np.int32), (3, 1)))
 
 
-@pytest.mark.parametrize("R,Lk", [(32, 200000), (3, 70001), (100, 16384)])
+@pytest.mark.parametrize("R,Lk", [(32, 200000), (3, 70001), (100, 16384), (1, 1000000)])
 def test_split_rows(R, Lk):
     """Few long rows: the split path (bounds per split, candidate collection, per-row select)."""
     rng = np.random.default_rng(R + Lk)
