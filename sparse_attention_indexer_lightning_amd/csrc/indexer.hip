@@ -30,12 +30,12 @@
 //    (a later key equal to it has a larger index and can never win, so ">"
 //    is exact);
 //  * binned (one query row per wavefront): a 256-bin histogram of the
-//    buffered keys, log-spaced above a base key (finest just above it) and
-//    kept current by the appends, gives the bin holding the k-th largest key
-//    directly; the filter keeps every entry at or above that bin's lower edge
-//    (at least k entries, all of them better than anything dropped), which
-//    then bounds the threshold.  The histogram is rebuilt from the threshold
-//    when the cut's bin is too full; exact selection is the fallback.
+//    buffered keys, log-spaced above the buffer's smallest key (finest just
+//    above it, where the cut falls when the buffer is full), gives the bin
+//    holding the k-th largest key; the filter keeps every entry at or above
+//    that bin's lower edge (at least k entries, all of them better than
+//    anything dropped), which then bounds the threshold.  Exact selection is
+//    the fallback when the cut's bin is too full.
 // With one row per wavefront, compactions are batched at the block barrier:
 // when any row must compact, every row past half its slack compacts too, so
 // waves stall on each other's compactions far less often.  At the end the
@@ -567,15 +567,16 @@ __device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, 
 }
 
 // Binned-selection state of one row (wave-uniform, one row per wavefront).
-// Once `binned`, the wave's 256-bin histogram counts every buffered key by
-// its bin above the window base `lo` (log-spaced bins, see bin_of); appends
-// keep it current, so a compaction reads the cut off it directly.
+// A compaction builds the wave's 256-bin histogram of the buffered keys by
+// their bin above the base `lo` (log-spaced bins, see bin_of) and reads the
+// cut off it.  (With a sampled starting threshold a row compacts only a few
+// times, so building the histogram then is cheaper than keeping it current
+// through every append.)
 struct BinState {
     int cnt;          // entries in the buffer
     uint32_t thr;     // append filter: key > thr
     float thr_f;      // the same filter on scores: score > thr_f
     uint32_t lo;      // histogram base (<= every buffered key)
-    bool binned;      // the histogram is live
 };
 
 // Largest float whose order-preserving key is <= thr: for every finite f,
@@ -618,7 +619,6 @@ __device__ void rebuild_hist(const uint32_t *bkey, BinState &st, uint32_t lo, ui
         for (int j = 0; j < 4; ++j) atomicAdd(&hist[e0 + j < st.cnt ? bin_of(kk[j], lo) : 256u + lane], 1u);
     }
     wave_lds_order();
-    st.binned = true;
 }
 
 template <typename IdxT>
@@ -639,43 +639,30 @@ __device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, u
     const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane);
     st.thr = theta;
     st.thr_f = key_floor_float(theta);
-    rebuild_hist<IdxT>(bkey, st, theta, hist, lane);
 }
 
-// Shrink the buffer off the live histogram: the bin holding the k-th largest
+// Shrink the buffer off a histogram of it: the bin holding the k-th largest
 // key is read off it, every entry at or above that bin's lower edge is kept
-// (at least k entries, all better than anything dropped), the emptied bins
-// are cleared, and the edge bounds the threshold.  Bins are log-spaced above
-// the base; once the cut has climbed into the coarser bins the histogram is
-// rebuilt from the new threshold, and when the cut's bin holds too many
-// entries (too little room freed) it is rebuilt from the current threshold
-// and read again; exact selection is the last resort.
+// (at least k entries, all better than anything dropped), and the edge
+// bounds the threshold.  Bins are log-spaced above the buffer's smallest key;
+// when the cut's bin holds too many entries (too little room freed), exact
+// selection takes over.
 // Precondition: st.cnt >= k.
 template <typename IdxT>
 __device__ __forceinline__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
                                uint32_t *pad_k, IdxT *pad_i, int lane) {
-    if (!st.binned) rebuild_hist<IdxT>(bkey, st, buffer_min<IdxT>(bkey, st.cnt, lane), hist, lane);
-    for (int attempt = 0;; ++attempt) {
-        int bstar;
-        uint32_t above;
-        hist_find(hist, k, lane, bstar, above);
-        const uint32_t nkeep = above + hist[bstar];
-        wave_lds_order();
-        if (bstar > 0 && (int)nkeep <= cap - 2 * KB) {
-            const uint32_t edge = st.lo + bin_floor(bstar);   // keep keys >= edge
-            st.cnt = filter_gt<IdxT>(bkey, bidx, st.cnt, edge - 1u, pad_k, pad_i, lane);
-            st.thr = edge - 1u;
-            st.thr_f = key_floor_float(st.thr);
-            if (bstar >= 96) {
-                rebuild_hist<IdxT>(bkey, st, st.thr, hist, lane);   // re-centre: finest bins at the cut
-            } else {
-                for (int j = lane; j < bstar; j += kWave) hist[j] = 0;
-                wave_lds_order();
-            }
-            return;
-        }
-        if (attempt > 0 || st.thr <= st.lo) break;
-        rebuild_hist<IdxT>(bkey, st, st.thr, hist, lane);   // finer bins just above the threshold
+    rebuild_hist<IdxT>(bkey, st, buffer_min<IdxT>(bkey, st.cnt, lane), hist, lane);
+    int bstar;
+    uint32_t above;
+    hist_find(hist, k, lane, bstar, above);
+    const uint32_t nkeep = above + hist[bstar];
+    wave_lds_order();
+    if (bstar > 0 && (int)nkeep <= cap - 2 * KB) {
+        const uint32_t edge = st.lo + bin_floor(bstar);   // keep keys >= edge
+        st.cnt = filter_gt<IdxT>(bkey, bidx, st.cnt, edge - 1u, pad_k, pad_i, lane);
+        st.thr = edge - 1u;
+        st.thr_f = key_floor_float(st.thr);
+        return;
     }
     compact_exact<IdxT>(bkey, bidx, st, k, hist, lane);
 }
@@ -796,7 +783,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     if (tid < 4) flags[tid] = 0;   // words 0-2: compaction requests; word 3: the sample failed
     BinState st;
-    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u; st.binned = false;
+    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u;
     const int want_level = p.topk + (p.cap - p.topk) / 2;
 
     // stage key block 0.  Thread tid stages 16-byte chunks tid + c*blockDim
@@ -848,7 +835,6 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 bk[at] = key;
                 bi[at] = (IdxT)s;
             }
-            if (st.binned) atomicAdd(&hist[cand ? bin_of(key, st.lo) : 256u + lane], 1u);
             st.cnt += __popcll(m);
         }
         return st.cnt > p.cap - KB;
@@ -865,7 +851,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     };
     auto compact_if_flagged = [&](int it) {
         if constexpr (kBinned) {
-            if (flags[it % 3] && st.cnt > want_level) {
+            if (st.cnt > want_level && flags[it % 3]) {
                 compact_binned<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, st, p.topk,
                                      p.cap, hist, bkey_all + (size_t)R * p.cap, bidx_all + (size_t)R * p.cap, lane);
             }
@@ -955,7 +941,6 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             st.thr = thr;
             st.thr_f = key_floor_float(thr);
             st.lo = 0u;
-            st.binned = false;
         };
         for (;;) {
         const int niter = ns + nblk;
@@ -1051,7 +1036,6 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         st.thr = 0u;
         st.thr_f = -INFINITY;
         st.lo = 0u;
-        st.binned = false;
         ns = 0;
         __syncthreads();
         }
