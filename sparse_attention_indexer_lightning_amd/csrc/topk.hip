@@ -14,10 +14,11 @@
 //     per-thread top-4 lists, a subset of the split).  At least m keys of the
 //     split are >= b_s, so at least S*m >= k keys of the row are >= min_s b_s:
 //     theta = min_s b_s never exceeds the row's k-th largest key;
-//  2. collect: every split writes its keys >= theta, in index order, to its
-//     own region of the workspace;
-//  3. select: one workgroup per row loads the candidates of all splits (in
-//     split order, so in index order) into LDS and runs the exact selection.
+//  2. collect: each quarter of a split (one wavefront) writes its keys >=
+//     theta, in index order, to its own region of the workspace;
+//  3. select: one workgroup per row loads the candidates of all regions (in
+//     split and quarter order, so in index order) into LDS and runs the
+//     exact selection.
 // Otherwise one workgroup (16 wavefronts) handles a whole row:
 //  1. bound: every thread keeps the 4 largest keys of its strided share of
 //     the row; the k-th largest of these 4096 keys is <= the row's k-th
@@ -181,9 +182,10 @@ constexpr int kSplitThreads = 256;
 constexpr int kSplitWaves = kSplitThreads / kWave;
 constexpr int kMinSplit = 4096;        // keys per split at least
 constexpr int kSplitTarget = 512;      // aim for about this many workgroups in total
-constexpr int kSplitVec = 16;          // keys per thread per step
-constexpr int kCollectSteps = 4;       // collect: steps whose loads are issued together
-static_assert(kSplitTarget <= 8 * kWave, "split offsets: eight per lane of one wavefront");
+constexpr int kSplitVec = 16;          // keys per thread per step (bound pass)
+constexpr int kCollectVec = 32;        // collect: keys per lane whose loads are issued together
+constexpr int kRegions = kSplitWaves;  // candidate regions per split: one per collect wavefront
+static_assert(kSplitTarget * kRegions <= 2 * kThreads, "region offsets: two per select thread");
 
 
 struct SplitPlan {
@@ -204,8 +206,8 @@ __host__ inline SplitPlan split_plan(int R, int Lk) {
 
 struct SplitWs {
     uint32_t *bound;     // [R][S]
-    int *count;          // [R][S]
-    uint2 *cand;         // [R][S][N]: (key, index)
+    int *count;          // [R][S][kRegions]
+    uint2 *cand;         // [R][S][kRegions][N / kRegions]: (key, index)
     size_t bytes;
 };
 
@@ -217,7 +219,7 @@ __host__ __device__ inline SplitWs split_ws(void *base, int R, const SplitPlan &
     w.bound = reinterpret_cast<uint32_t *>(p + off);
     off += (rs * 4 + 255) & ~(size_t)255;
     w.count = reinterpret_cast<int *>(p + off);
-    off += (rs * 4 + 255) & ~(size_t)255;
+    off += (rs * kRegions * 4 + 255) & ~(size_t)255;
     w.cand = reinterpret_cast<uint2 *>(p + off);
     off += rs * pl.N * 8;
     w.bytes = off;
@@ -259,65 +261,44 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_bound(TopkArgs a, Sp
 }
 
 // 2. per split: keys >= theta = min over the row's bounds, in index order.
-// Each step thread t looks at keys c0 + e * 256 + t (e < kSplitVec), so the
-// order is e-major; a per-(e, wave) count table gives every key its slot.
-// The loads of kCollectSteps steps are issued together and consumed in
-// order, so a split costs about one memory latency rather than one per step.
+// Wavefront w of a split takes the w-th quarter of its keys (N is a multiple
+// of 256) and appends its candidates, in index order, to a region of its own
+// (ballot + lane prefix per 64 keys): no block-wide ordering, so no barriers.
+// The regions of a row, in (split, wavefront) order, are in index order.
 __global__ __launch_bounds__(kSplitThreads) void topk_split_collect(TopkArgs a, SplitPlan pl, SplitWs ws) {
-    __shared__ uint32_t wcnt[2][kSplitVec][kSplitWaves];
     const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int n = row_valid(a, r);
-    const int j0 = s * pl.N, j1 = min(j0 + pl.N, n);
-    uint32_t tmin = 0xFFFFFFFFu;   // theta: every lane loads some bounds, then a wave minimum
-    for (int i = lane; i < pl.S; i += kWave) tmin = min(tmin, ws.bound[(size_t)r * pl.S + i]);
-    const uint32_t theta = ~wave_max32(~tmin);
+    const int q = pl.N / kRegions;
+    const int j0 = s * pl.N + wave * q, j1 = min(j0 + q, n);
     const float *row = a.scores + (size_t)r * a.Lk;
-    uint2 *out = ws.cand + ((size_t)r * pl.S + s) * pl.N;
-    constexpr int kChunk = kCollectSteps * kSplitVec * kSplitThreads;
-    uint32_t base = 0;
-    int par = 0;
-    for (int c1 = j0; c1 < j1; c1 += kChunk) {
-        float v[kCollectSteps * kSplitVec];
+    float v[kCollectVec];
+    auto load_chunk = [&](int c0) {
 #pragma unroll
-        for (int e = 0; e < kCollectSteps * kSplitVec; ++e) {
-            const int j = c1 + e * kSplitThreads + tid;
+        for (int e = 0; e < kCollectVec; ++e) {
+            const int j = c0 + e * kWave + lane;
             v[e] = j < j1 ? row[j] : -INFINITY;
         }
+    };
+    // the first chunk's loads go out before theta's (bounds, then a wave minimum)
+    load_chunk(j0);
+    uint32_t tmin = 0xFFFFFFFFu;
+    for (int i = lane; i < pl.S; i += kWave) tmin = min(tmin, ws.bound[(size_t)r * pl.S + i]);
+    const uint32_t theta = ~wave_max32(~tmin);
+    uint2 *out = ws.cand + ((size_t)r * pl.S + s) * pl.N + (size_t)wave * q;
+    uint32_t cnt = 0;
+    for (int c0 = j0; c0 < j1; c0 += kCollectVec * kWave) {
+        if (c0 != j0) load_chunk(c0);
 #pragma unroll
-        for (int q = 0; q < kCollectSteps; ++q) {
-            const int c0 = c1 + q * kSplitVec * kSplitThreads;
-            if (c0 >= j1) break;
-            uint32_t u[kSplitVec];
-            uint64_t B[kSplitVec];
-#pragma unroll
-            for (int e = 0; e < kSplitVec; ++e) {
-                const int j = c0 + e * kSplitThreads + tid;
-                u[e] = score_key(v[q * kSplitVec + e]);
-                B[e] = ballot(j < j1 && u[e] >= theta);
-                if (lane == 0) wcnt[par][e][wave] = (uint32_t)__popcll(B[e]);
-            }
-            __syncthreads();
-            uint32_t before = base;   // keys kept ahead of (e, wave) in this step
-#pragma unroll
-            for (int e = 0; e < kSplitVec; ++e) {
-                uint32_t tot = 0, wb = 0;
-#pragma unroll
-                for (int w = 0; w < kSplitWaves; ++w) {
-                    const uint32_t c = wcnt[par][e][w];
-                    if (w < wave) wb += c;
-                    tot += c;
-                }
-                if ((B[e] >> lane) & 1u) {
-                    const int j = c0 + e * kSplitThreads + tid;
-                    out[before + wb + (uint32_t)lanes_below(B[e])] = make_uint2(u[e], (uint32_t)j);
-                }
-                before += tot;
-            }
-            base = before;
-            par ^= 1;
+        for (int e = 0; e < kCollectVec; ++e) {
+            const int j = c0 + e * kWave + lane;
+            const uint32_t u = score_key(v[e]);
+            const bool keep = j < j1 && u >= theta;
+            const uint64_t B = ballot(keep);
+            if (keep) out[cnt + (uint32_t)lanes_below(B)] = make_uint2(u, (uint32_t)j);
+            cnt += (uint32_t)__popcll(B);
         }
     }
-    if (tid == 0) ws.count[(size_t)r * pl.S + s] = (int)base;
+    if (lane == 0) ws.count[((size_t)r * pl.S + s) * kRegions + wave] = (int)cnt;
 }
 
 // 3. per row: exact selection over all splits' candidates.
@@ -332,52 +313,51 @@ __global__ __launch_bounds__(kThreads) void topk_split_select(TopkArgs a, SplitP
         for (int j = tid; j < k; j += kThreads) out[j] = j < n ? j : -1;
         return;
     }
-    // offsets of the splits' candidate lists (split order is index order):
-    // one wavefront loads every count at once, eight per lane, and scans them
-    int *soff = reinterpret_cast<int *>(sh.ukey);   // [S + 1]; ukey is unused here
-    const int S = pl.S;
-    if (tid < kWave) {
-        int c[8], sum = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = 8 * tid + e;
-            c[e] = i < S ? ws.count[(size_t)r * S + i] : 0;
-            sum += c[e];
-        }
+    // offsets of the candidate regions, (split, wavefront) order being index
+    // order: two counts per thread, a wavefront scan, then the wavefront totals
+    int *soff = reinterpret_cast<int *>(sh.ukey);   // [nreg + 1]; ukey is unused here
+    const int nreg = pl.S * kRegions;
+    const int q = pl.N / kRegions;
+    {
+        const int wave = tid / kWave, lane = tid % kWave;
+        const int i0 = 2 * tid;
+        const int c0 = i0 < nreg ? ws.count[(size_t)r * nreg + i0] : 0;
+        const int c1 = i0 + 1 < nreg ? ws.count[(size_t)r * nreg + i0 + 1] : 0;
+        const int sum = c0 + c1;
         int incl = sum;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
             const int t = __shfl_up(incl, d, kWave);
-            if (tid >= d) incl += t;
+            if (lane >= d) incl += t;
         }
-        int run = incl - sum;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = 8 * tid + e;
-            if (i < S) soff[i] = run;
-            run += c[e];
-        }
-        if (tid == kWave - 1) soff[S] = incl;
+        if (lane == kWave - 1) sh.wtot[0][wave] = (uint32_t)incl;
+        __syncthreads();
+        int woff = 0;
+        for (int w = 0; w < wave; ++w) woff += (int)sh.wtot[0][w];
+        const int ex = woff + incl - sum;
+        if (i0 < nreg) soff[i0] = ex;
+        if (i0 + 1 < nreg) soff[i0 + 1] = ex + c0;
+        if (tid == kThreads - 1) soff[nreg] = ex + sum;
     }
     __syncthreads();
-    const int total = soff[S];
+    const int total = soff[nreg];
     if (total <= kCandCap) {
-        // gather the candidates of every split: candidate g of the row is
-        // entry g - soff[i] of the last split i with soff[i] <= g; each thread
-        // issues all its loads before storing any
+        // gather the candidates of every region: candidate g of the row is
+        // entry g - soff[i] of the last region i with soff[i] <= g; each
+        // thread issues all its loads before storing any
         constexpr int kPer = kCandCap / kThreads;
         uint2 v[kPer];
 #pragma unroll
         for (int e = 0; e < kPer; ++e) {
             const int gi = tid + e * kThreads;
             if (gi < total) {
-                int lo = 0, hi = S - 1;
+                int lo = 0, hi = nreg - 1;
                 while (lo < hi) {
                     const int mid = (lo + hi + 1) >> 1;
                     if (soff[mid] <= gi) lo = mid;
                     else hi = mid - 1;
                 }
-                v[e] = ws.cand[((size_t)r * S + lo) * pl.N + (gi - soff[lo])];
+                v[e] = ws.cand[(size_t)r * pl.S * pl.N + (size_t)lo * q + (gi - soff[lo])];
             }
         }
 #pragma unroll

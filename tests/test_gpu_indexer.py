@@ -93,6 +93,8 @@ def test_head_counts_and_dims(enc, H, D):
     (1, 200, 200, 1),       # k = 1
     (2, 3, 5000, 300),      # decode-shaped (split-key path) with B > 1, Lq > 1
     (1, 1, 3000, 2048),     # single decode query
+    (2, 300, 6000, 2048),   # sampled starting threshold, batch, queries at the end of the context
+    (1, 64, 5000, 512),     # sampled threshold with a smaller k (rank r = 40 of the sample)
 ])
 def test_edge_shapes_fp8(B, Lq, Lk, topk):
     wl = inputs.Workload("e", B, Lq, Lk, 64, 128, topk, "fp8", "bf16", 5)
@@ -199,3 +201,19 @@ def test_sampled_threshold_fallback():
     to, so = indexer_oracle(q, k, w, topk, rows=rows)
     check_scores(sg[rows], so, RTOL["fp8"], "sampled fallback")
     check_index_sets(tg[rows], to, so, pos[rows], topk, RTOL["fp8"], "sampled fallback")
+
+
+@pytest.mark.parametrize("kind", ["ties", "reverse"])
+def test_sampled_threshold_closed_forms(kind):
+    """Long rows with k = 2048 take the sampled starting threshold.  With every
+    score equal the threshold is the tie value itself, no key beats it, and
+    the workgroups sweep again without the sample (ties then go to the lowest
+    indices); with I = -s the sample's threshold admits exactly the keys
+    below the r-th sampled one."""
+    Lq, Lk, k = 16, 6000, 2048
+    q, kk, w = inputs.closed_form_indexer(1, Lk, 64, 128, "fp8", kind, device=DEV)
+    q = q[:, Lk - Lq:].contiguous()
+    w = w[:, Lk - Lq:].contiguous()
+    t, _ = run_full(q, kk, w, k)
+    tg = t.cpu().numpy().reshape(Lq, k)
+    assert np.array_equal(tg, np.tile(np.arange(k, dtype=np.int32), (Lq, 1))), kind
