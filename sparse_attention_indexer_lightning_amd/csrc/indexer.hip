@@ -1214,15 +1214,21 @@ struct ScoreParams {
 
 constexpr int kDecodeWaves = 4;
 constexpr int kComputeUnits = 256;   // MI355X
+// Score rows of key ranges up to this many keys are staged in LDS and written
+// in one burst at the end of the workgroup (two workgroups per compute unit
+// still fit): writes spread through the sweep cost far more than their bytes
+// when they mix into the saturating read stream of the keys.
+constexpr int kDecodeStageMaxKeys = 16384;
 
 // 64 heads of one query against a contiguous key range; B operands are read
 // straight from HBM (each key is used by exactly one query row here).
-template <Enc E, int D, bool Paged>
+template <Enc E, int D, bool Paged, bool Stage = false>
 __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_scores_kernel(ScoreParams p) {
     using S = Shape<E, D>;
     constexpr int H = 64;
     __shared__ BoundShared bsh;
+    extern __shared__ __align__(16) float sstage[];   // Stage: the range's scores
     uint32_t top[kLocal] = {0u, 0u, 0u, 0u};   // this thread's 4 largest keys (bound)
     const int tid = threadIdx.x, lane = tid % kWave, g = lane >> 4, n = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -1305,10 +1311,14 @@ void decode_scores_kernel(ScoreParams p) {
                 }
             }
         };
+        auto put = [&](int s, float v) {   // s < s1
+            if constexpr (Stage) sstage[s - s0] = v;
+            else out[s] = v;
+        };
         auto score_block = [&](const v8i (&B)[2][2], int base) {
             const float sc = score64_mfma32_b(Q32f, B);
             const int s = base + lane;
-            if (s < s1) out[s] = s <= pos ? sc : -INFINITY;
+            if (s < s1) put(s, s <= pos ? sc : -INFINITY);
             if (s < s1 && s <= pos) keep_top4(top, score_key(sc));
         };
         const int last = min(s1, pos + 1);        // keys at or before the query position
@@ -1338,7 +1348,18 @@ void decode_scores_kernel(ScoreParams p) {
         }
         for (; base < s1; base += STRIDE) {
             const int s = base + lane;
-            if (s < s1) out[s] = -INFINITY;
+            if (s < s1) put(s, -INFINITY);
+        }
+        if constexpr (Stage) {
+            // one burst of 16-byte stores (the score row stride and s0 are
+            // multiples of 4 floats when staging is chosen)
+            __syncthreads();
+            const int len = s1 - s0;
+            for (int i = 4 * (int)threadIdx.x; i < len; i += 4 * kDecodeWaves * kWave) {
+                if (i + 4 <= len) *reinterpret_cast<v4f *>(out + s0 + i) = *reinterpret_cast<const v4f *>(sstage + i);
+                else
+                    for (int e = i; e < len; ++e) out[s0 + e] = sstage[e];
+            }
         }
         write_bound();
         return;
@@ -1485,6 +1506,33 @@ hipError_t launch_decode_d(const IndexerArgs &a, hipStream_t st, const PagedKeys
     decode_split_geometry(a, &nsplit, &p.split);
     p.bound = a.split_bound;
     p.topk = a.topk;
+    if constexpr (E == Enc::FP8 && D == 128) {
+        if (p.split <= kDecodeStageMaxKeys && a.Lk % 4 == 0) {
+            const size_t lds = (size_t)p.split * sizeof(float);
+            if (pk) {
+                p.block_table = pk->block_table;
+                p.row_info = reinterpret_cast<const int2 *>(pk->row_info);
+                p.bs_log2 = pk->bs_log2;
+                p.max_blocks = pk->max_blocks;
+                p.num_blocks = pk->num_blocks;
+                auto kern = decode_scores_kernel<E, D, true, true>;
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL(kern, dim3((unsigned)nsplit, (unsigned)(a.B * a.Lq)), dim3(kDecodeWaves * kWave), lds, st, p);
+            } else {
+                p.block_table = nullptr;
+                p.row_info = nullptr;
+                p.bs_log2 = p.max_blocks = p.num_blocks = 0;
+                auto kern = decode_scores_kernel<E, D, false, true>;
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL(kern, dim3((unsigned)nsplit, (unsigned)(a.B * a.Lq)), dim3(kDecodeWaves * kWave), lds, st, p);
+            }
+            return hipGetLastError();
+        }
+    }
     if (pk) {
         p.block_table = pk->block_table;
         p.row_info = reinterpret_cast<const int2 *>(pk->row_info);
