@@ -57,11 +57,11 @@ constexpr int kPadEntries = 256; // candidate-buffer padding read by 4-per-lane 
 constexpr int kHistWords = 320;  // 256 bins + one dummy slot per lane for masked-off updates
 // Sampled starting threshold of the 64-head sweep: every kSampleStride-th key
 // block is scored first; a row's threshold is then its sample's r-th largest
-// key, r = kSampleMargin * k * (sampled keys) / (keys), unless r is below
+// key, r = ceil(7/4 * k * (sampled keys) / (keys)), unless r is below
 // kSampleMinRank or above the sample.  Only workgroups with at least
 // kSampleMinBlocks key blocks sample.
 constexpr int kSampleStride = 32;
-constexpr int kSampleMargin = 2;
+constexpr int kSampleMarginNum = 7, kSampleMarginDen = 4;   // 7/4
 constexpr int kSampleMinRank = 32;
 constexpr int kSampleMinBlocks = 64;
 
@@ -916,9 +916,11 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         // at least k entries, its k-th largest key is above tau and every
         // key that tau filtered out lies below it: the result is exact.  A
         // row left with fewer than k entries makes its workgroup sweep again
-        // without the sample.  For i.i.d. scores r is about 2k/32 = 128 and a
-        // shortfall is a many-sigma event; a row then appends about 2k keys
-        // instead of k(1 + ln(n/k)), and compacts a few times instead of ~16.
+        // without the sample.  For i.i.d. scores r is about 7k/128 = 112: the
+        // number of keys above tau is about 7k/4 with a relative spread of
+        // 1/sqrt(r) (9.4 %), so a shortfall below k is a 4.5-sigma event
+        // (about one row in 300,000); a row then appends about 7k/4 keys
+        // instead of k(1 + ln(n/k)), and compacts once or twice instead of ~16.
         int ns = nblk >= kSampleMinBlocks ? (nblk - 1) / kSampleStride + 1 : 0;
         auto bmap = [&](int it) { return it < ns ? it * kSampleStride : it - ns; };
         auto tau_step = [&]() {
@@ -930,7 +932,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 const int lo = j * kSampleStride * KB;
                 if (lo <= pos) nsk += min(KB, pos + 1 - lo);
             }
-            const int r = (int)(((long long)kSampleMargin * p.topk * nsk + pos) / (pos + 1));
+            const long long den = (long long)kSampleMarginDen * (pos + 1);
+            const int r = (int)(((long long)kSampleMarginNum * p.topk * nsk + den - 1) / den);
             uint32_t thr = 0u;   // 0: no filter
             if (r >= kSampleMinRank && r <= st.cnt) {
                 int c = st.cnt;
