@@ -37,8 +37,8 @@
 //    anything dropped), which then bounds the threshold.  Exact selection is
 //    the fallback when the cut's bin is too full.
 // With one row per wavefront, compactions are batched at the block barrier:
-// when any row must compact, every row past half its slack compacts too, so
-// waves stall on each other's compactions far less often.  At the end the
+// when any row must compact, every row past a quarter of its slack compacts
+// too, so waves stall on each other's compactions far less often.  At the end the
 // exact selection leaves min(k, p+1) entries, already in ascending order.
 #include <algorithm>
 #include <type_traits>
@@ -784,7 +784,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     if (tid < 4) flags[tid] = 0;   // words 0-2: compaction requests; word 3: the sample failed
     BinState st;
     st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u;
-    const int want_level = p.topk + (p.cap - p.topk) / 2;
+    const int want_level = p.topk + (p.cap - p.topk) / 4;   // past a quarter of the slack
 
     // stage key block 0.  Thread tid stages 16-byte chunks tid + c*blockDim
     // (c < cpt).  Keys past Lk are clamped to the last key: their scores lie
@@ -842,7 +842,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // Compaction requests of iteration it: word it%3 collects them; word
     // (it+1)%3 was last read before the previous barrier and is next written
     // after this one.  After the barrier every requesting row compacts, and so
-    // does every row past half its slack.
+    // does every row past a quarter of its slack.
     auto raise_flags = [&](int it, bool need) {
         if constexpr (kBinned) {
             if (need && lane == 0) atomicOr(&flags[it % 3], 1);
