@@ -500,22 +500,43 @@ __global__ __launch_bounds__(256) void sparse_mla_merge_kernel(MlaWideArgs a) {
     if (w >= a.B * a.Lq * a.Hq) return;
     const int qrow = w / a.Hq, h = w % a.Hq;
     const float *pl = a.part_lse + (size_t)qrow * a.nchunk * a.Hq + h;
-    float mx = -INFINITY;
-    for (int c = 0; c < a.nchunk; ++c) mx = fmaxf(mx, pl[(size_t)c * a.Hq]);
+    const unsigned char *po = static_cast<const unsigned char *>(a.part_o) + ((size_t)qrow * a.nchunk * a.Hq + h) * DV * 2 +
+                              16 * lane;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    if (mx != -INFINITY) {
-        for (int c = 0; c < a.nchunk; ++c) {
-            const float lc = pl[(size_t)c * a.Hq];
-            if (lc == -INFINITY) continue;
-            const float wc = __builtin_amdgcn_exp2f(lc - mx);
-            wsum += wc;
-            const v4i v = *reinterpret_cast<const v4i *>(static_cast<const unsigned char *>(a.part_o) +
-                                                         (((size_t)qrow * a.nchunk + c) * a.Hq + h) * DV * 2 + 16 * lane);
+    auto add = [&](float wc, const v4i &v) {
+        wsum += wc;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                acc[2 * k] += wc * __uint_as_float((uint32_t)v[k] << 16);
-                acc[2 * k + 1] += wc * __uint_as_float((uint32_t)v[k] & 0xFFFF0000u);
+        for (int k = 0; k < 4; ++k) {
+            acc[2 * k] += wc * __uint_as_float((uint32_t)v[k] << 16);
+            acc[2 * k + 1] += wc * __uint_as_float((uint32_t)v[k] & 0xFFFF0000u);
+        }
+    };
+    float mx = -INFINITY;
+    constexpr int kMaxChunks = 8;
+    if (a.nchunk <= kMaxChunks) {
+        // every chunk's statistics and partial row are loaded before any is used
+        float lc[kMaxChunks];
+        v4i v[kMaxChunks];
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+            lc[c] = c < a.nchunk ? pl[(size_t)c * a.Hq] : -INFINITY;
+            v[c] = c < a.nchunk ? *reinterpret_cast<const v4i *>(po + (size_t)c * a.Hq * DV * 2) : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) mx = fmaxf(mx, lc[c]);
+        if (mx != -INFINITY) {
+#pragma unroll
+            for (int c = 0; c < kMaxChunks; ++c)
+                if (lc[c] != -INFINITY) add(__builtin_amdgcn_exp2f(lc[c] - mx), v[c]);
+        }
+    } else {
+        for (int c = 0; c < a.nchunk; ++c) mx = fmaxf(mx, pl[(size_t)c * a.Hq]);
+        if (mx != -INFINITY) {
+            for (int c = 0; c < a.nchunk; ++c) {
+                const float lc = pl[(size_t)c * a.Hq];
+                if (lc == -INFINITY) continue;
+                add(__builtin_amdgcn_exp2f(lc - mx), *reinterpret_cast<const v4i *>(po + (size_t)c * a.Hq * DV * 2));
             }
         }
     }
