@@ -94,7 +94,8 @@ def test_head_counts_and_dims(enc, H, D):
     (2, 3, 5000, 300),      # decode-shaped (split-key path) with B > 1, Lq > 1
     (1, 1, 3000, 2048),     # single decode query
     (2, 300, 6000, 2048),   # sampled starting threshold, batch, queries at the end of the context
-    (1, 64, 5000, 512),     # sampled threshold with a smaller k (rank r = 40 of the sample)
+    (1, 64, 5000, 512),     # sampled threshold with a smaller k (rank r = 35 of the sample)
+    (2, 2, 4097, 512),      # decode-shaped, score rows not a multiple of 4 floats (scores written directly)
 ])
 def test_edge_shapes_fp8(B, Lq, Lk, topk):
     wl = inputs.Workload("e", B, Lq, Lk, 64, 128, topk, "fp8", "bf16", 5)
