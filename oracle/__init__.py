@@ -23,8 +23,13 @@ Sources (page title and section):
         allocation)
 
 Parity status of each function (pins live in tests/test_oracle_*.py):
-  indexer_scores   pinned (hand-worked 8-token example, closed forms, H=1 case vs numpy)
-  topk             pinned (brute force vs full sort and repeated argmax, closed forms)
+  indexer_scores   pinned (hand-worked 8-token example; recency / reverse / tie
+                   closed forms; a B = 3, Lq < Lk closed form with distinct keys
+                   per sequence and scrambled row order; the H = 1 case vs numpy;
+                   non-integer scores against the exact rational value rounded
+                   to the nearest fp32 by brute force, ties to even)
+  topk             pinned (brute force vs full sort and repeated argmax, closed
+                   forms, rows with no valid key)
   route            pinned (hand-worked example, invariants)
   sparse_mla       pinned (dense attention via torch SDPA on CPU, closed forms)
   overlap          pinned (hand-worked rows, identical / disjoint / nested sets, symmetry)
@@ -33,9 +38,14 @@ Parity status of each function (pins live in tests/test_oracle_*.py):
                    pinned (one sequence over an identity table = the contiguous
                    oracle; page permutations change nothing; a batch = its
                    sequences taken one at a time)
-  stack            parity unpinned: the way layers compose (residual add of the
-                   head-summed attention output, then the seeded FFN stand-in)
-                   is a reading, not something the pages fix.
+  stack            pinned (hand-worked two-layer example, Full/Shared second
+                   layer x plain/residual FFN, exact integer values).  The way
+                   layers compose (per-layer inputs independent of X, residual
+                   add of the head-summed attention output, then the seeded FFN
+                   stand-in) is a reading of the pages' inference loop; the pin
+                   fixes that this code computes that reading.
+  codecs           pinned (every fp8 / bf16 code vs torch; bf16 and fp32
+                   rounding vs brute-force nearest search)
 """
 from __future__ import annotations
 
@@ -279,7 +289,7 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def stack(pattern: str, x0_bits: np.ndarray, layers, topk_k: int, sm_scale: float, Dv: int,
           residual_ffn: bool, nthreads=None):
     """Layer stack of the inference loop in [ITO] § "Einfache Implementierung, enorme
-    Effizienzgewinne" (parity unpinned composition, see module docstring).
+    Effizienzgewinne" (the composition is a reading; see module docstring).
 
     layers[l] holds seeded inputs: q_i, k_i, w (indexer, with 'idx_dtypes'),
     q, kv (attention, bf16 bits) and W (FFN stand-in, bf16 bits [Dm, Dm]).

@@ -283,3 +283,136 @@ def test_topk_invariants_random_rows():
             chosen = s[r, row]
             rest = np.delete(s[r, : pos[r] + 1], row)
             assert chosen.min() >= rest.max()
+
+
+def test_topk_row_with_no_valid_key():
+    """pos = -1 means the row has no key: the index set is empty, all padding."""
+    s = np.array([[3.0, 1.0, 2.0], [3.0, 1.0, 2.0], [3.0, 1.0, 2.0]], np.float32)
+    pos = np.array([-1, 0, 2], np.int32)
+    t = oracle.topk(s, pos, 2)
+    assert t.tolist() == [[-1, -1], [0, -1], [0, 2]]
+
+
+# ------------------------------------------------------------ batches, Lq < Lk
+
+def _batched_closed_form(enc):
+    """B = 3 sequences of Lk = 40 keys, Lq = 5 queries each (positions 35..39).
+    Keys of sequence b hold the base-8 digits of v = s + 100 b; head 0 of query
+    (b, i) is a*(1, 8, 64) on digits 0-2, head 1 is a*(1, 8, 64) on digits 3-5,
+    a = 1 + (b + i) mod 3.  Head weights (1, 512) (sequence 1: (-1, -512)).
+    Then q_0.k = a (v mod 512), q_1.k = a (v div 512), both >= 0, so
+    I[(b, i), s] = +-a (s + 100 b) exactly for s <= 35 + i."""
+    B, Lq, Lk, H, D = 3, 5, 40, 2, 8
+    q = np.zeros((B, Lq, H, D), np.float32)
+    k = np.zeros((B, Lk, D), np.float32)
+    w = np.zeros((B, Lq, H), np.float32)
+    a = np.zeros((B, Lq))
+    for b in range(B):
+        for s in range(Lk):
+            v = s + 100 * b
+            for j in range(6):
+                k[b, s, j] = (v >> (3 * j)) & 7
+        for i in range(Lq):
+            a[b, i] = 1 + (b + i) % 3
+            q[b, i, 0, :3] = a[b, i] * np.array([1, 8, 64])
+            q[b, i, 1, 3:6] = a[b, i] * np.array([1, 8, 64])
+            w[b, i] = (-1.0, -512.0) if b == 1 else (1.0, 512.0)
+    if enc == "fp32":
+        return (q, k, w), ("fp32",) * 3, a
+    tq = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    tk = torch.from_numpy(k).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    tw = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy()
+    return (tq, tk, tw), ("fp8", "fp8", "bf16"), a
+
+
+@pytest.mark.parametrize("enc", ["fp32", "fp8"])
+def test_batched_rows_and_offset_positions(enc):
+    (q, k, w), dts, a = _batched_closed_form(enc)
+    B, Lq, Lk, topk = 3, 5, 40, 4
+    # every flat row, in a scrambled order, to pin row -> (b, i) as well
+    rows = np.array([7, 0, 14, 3, 10, 5, 12, 1, 9, 2, 13, 6, 11, 4, 8], np.int64)
+    t, s = oracle.indexer_topk(q, k, w, dts, topk, rows=rows)
+    for r, flat in enumerate(rows):
+        b, i = divmod(int(flat), Lq)
+        p = Lk - Lq + i
+        sign = -1.0 if b == 1 else 1.0
+        want = sign * a[b, i] * (np.arange(p + 1) + 100 * b)
+        assert np.array_equal(s[r, : p + 1], want.astype(np.float32)), (b, i)
+        assert np.all(np.isneginf(s[r, p + 1:])), (b, i)
+        exp_t = list(range(topk)) if b == 1 else list(range(p + 1 - topk, p + 1))
+        assert t[r].tolist() == exp_t, (b, i)
+
+
+# ------------------------------------------------------------ fp32 rounding
+
+def _f32_from_bits(u: int) -> float:
+    return float(np.array([u], dtype=np.uint32).view(np.float32)[0])
+
+
+def _nearest_f32_brute(x) -> float:
+    """Nearest fp32 to the exact rational x (ties to the even code), by
+    comparing exact distances to the neighbouring codes of a first guess."""
+    from fractions import Fraction
+    x = Fraction(x)
+    if x == 0:
+        return 0.0
+    guess = np.float32(float(x))
+    base = int(np.array([guess], dtype=np.float32).view(np.uint32)[0])
+    best = None
+    for u in range(base - 3, base + 4):
+        u &= 0xFFFFFFFF
+        v = _f32_from_bits(u)
+        if not math.isfinite(v):
+            continue
+        d = abs(Fraction(v) - x)
+        if best is None or d < best[0] or (d == best[0] and (u & 1) == 0 and (best[1] & 1) == 1):
+            best = (d, u)
+    return _f32_from_bits(best[1])
+
+
+def test_round_f32_nearest_even_against_brute_force():
+    rng = np.random.default_rng(17)
+    L = oracle.lib()
+    xs = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 38, 2000))
+    xs += list(rng.uniform(-4, 4, 500))                       # non-integer, mantissa bits beyond fp32
+    for u in [0x3F800000, 0x3F800001, 0x40490FDB, 0x00000001, 0x00800000, 0x7F7FFFFE, 0xBF800003]:
+        lo, hi = _f32_from_bits(u), _f32_from_bits(u + 1)
+        mid = (lo + hi) / 2.0                                  # exact in double: a tie
+        xs += [mid, mid + abs(mid) * 2.0 ** -40, mid - abs(mid) * 2.0 ** -40]
+    for x in xs:
+        got = L.or_round_f32(float(x))
+        want = _nearest_f32_brute(float(x))
+        assert np.float32(got).tobytes() == np.float32(want).tobytes(), x
+
+
+def test_scores_round_once_to_nearest_even():
+    """Non-integer scores: the exact value of sum_h w * max(0, q.k) (Python
+    fractions) rounded to the nearest fp32 by brute force.  Inputs have at
+    most 12 significant bits, so the exact score has at most ~40 and every
+    rounding direction (down, up, tie to even) occurs."""
+    from fractions import Fraction
+    rng = np.random.default_rng(23)
+    Lq, H, D = 24, 4, 6
+    q = (rng.integers(-2047, 2048, (1, Lq, H, D)) / 64.0).astype(np.float32)
+    k = (rng.integers(-2047, 2048, (1, Lq, D)) / 128.0).astype(np.float32)
+    w = (rng.integers(-2047, 2048, (1, Lq, H)) / 1024.0).astype(np.float32)
+    # crafted rows: q.k = 1 + 2^-11 + 2^-24 (a tie: even rounds down) and
+    # q.k = 1 + 2^-11 + 2^-23 + 2^-24 + 2^-35 (above the tie: rounds up)
+    q[0, 0] = 0.0; w[0, 0] = 0.0; q[0, 0, 0, 0] = 1 + 2.0 ** -12; w[0, 0, 0] = 1.0
+    q[0, 1] = 0.0; w[0, 1] = 0.0; q[0, 1, 0, 0] = 1 + 2.0 ** -12; w[0, 1, 0] = 1.0
+    k[0, 0] = 0.0; k[0, 0, 0] = 1 + 2.0 ** -12
+    k[0, 1] = 0.0; k[0, 1, 0] = 1 + 2.0 ** -12 + 2.0 ** -23
+    s = oracle.indexer_scores(q, k, w, ("fp32",) * 3)
+    assert s[0, 0] == np.float32(1 + 2.0 ** -11)
+    assert s[1, 1] == np.float32(1 + 2.0 ** -11 + 2.0 ** -22)
+    inexact = 0
+    for t in range(Lq):
+        for j in range(t + 1):
+            exact = Fraction(0)
+            for h in range(H):
+                dot = sum(Fraction(float(q[0, t, h, d])) * Fraction(float(k[0, j, d])) for d in range(D))
+                exact += Fraction(float(w[0, t, h])) * max(dot, Fraction(0))
+            want = _nearest_f32_brute(exact)
+            inexact += Fraction(want) != exact
+            assert np.float32(s[t, j]).tobytes() == np.float32(want).tobytes(), (t, j, float(exact))
+    assert inexact > 100   # the pin exercises rounding, not just exact sums
