@@ -146,8 +146,8 @@ idxc_status idx_cache_route(const char *pattern, int layer, const idxc_indexer_d
  *   q   bf16 [B, Lq, Hq, Dqk]
  *   kv  bf16 [B, Lk, Dqk]   latent rows; keys are the whole row, values are
  *                           its first Dv columns
- *   t   int32 [B, Lq, topk] row indices into kv (entries < 0 are skipped;
- *                           entries must be < Lk)
+ *   t   int32 [B, Lq, topk] row indices into kv (entries < 0 or >= Lk are
+ *                           skipped: they select no row)
  *   out bf16 [B, Lq, Hq, Dv]:  out[h] = sum_j softmax_j(z) kv[t_j, :Dv],
  *                           z_j = sm_scale * q[h] . kv[t_j]   (fp32 math)
  *   lse optional fp32 [B, Lq, Hq]: log-sum-exp of z (-inf, with out = 0,

@@ -286,39 +286,70 @@ def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out.reshape(np.shape(x))
 
 
+def stack_layer(x_bits: np.ndarray, t_cache: np.ndarray, lay, sm_scale: float, Dv: int, residual_ffn: bool,
+                rows=None, nthreads=None, detail=False):
+    """One layer of the stack after routing (the attention and FFN steps of the
+    inference loop in [ITO] § "Einfache Implementierung, enorme
+    Effizienzgewinne"), X kept in bf16 between steps:
+      O = SparseMLA(q, kv, T) -> X1 = bf16(X + pad(sum_h O))
+        -> X = bf16(X1 W)  (plain linear map), or X = bf16(X1 + X1 W)  (``residual_ffn``).
+    x_bits bf16 bits [n, Dm] holds the rows listed in ``rows`` (default: all L
+    rows, in order); lay["q"] holds the attention queries of those same rows,
+    [1, n, Hq, Dqk]; t_cache [1, L, k] is the whole index cache.
+    Returns (X bf16 bits [n, Dm], O bf16 bits [n, Hq, Dv]) and, with ``detail``,
+    the values each of the two bf16 roundings was applied to (float64 [n, Dm]:
+    "pre_x1" = X + pad(sum_h O), "pre_x" = X1 W or X1 + X1 W)."""
+    x = bf16_bits_to_f64(x_bits)
+    n, Dm = x.shape
+    L = t_cache.shape[1]
+    rows = np.arange(L, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    assert rows.size == n
+    t_rows = np.ascontiguousarray(t_cache.reshape(L, -1)[rows])[None]
+    o_bits, _ = sparse_mla_dv(lay["q"], lay["kv"], t_rows, sm_scale, Dv, nthreads=nthreads)
+    o = bf16_bits_to_f64(o_bits).reshape(n, -1, Dv).sum(axis=1)
+    upd = np.zeros((n, Dm))
+    upd[:, :Dv] = o
+    pre_x1 = x + upd
+    x1 = bf16_bits_to_f64(f64_to_bf16_bits(pre_x1))
+    y = x1 @ bf16_bits_to_f64(lay["W"])
+    pre_x = x1 + y if residual_ffn else y
+    out = (f64_to_bf16_bits(pre_x), o_bits.reshape(n, -1, Dv))
+    return out + ({"pre_x1": pre_x1, "pre_x": pre_x},) if detail else out
+
+
 def stack(pattern: str, x0_bits: np.ndarray, layers, topk_k: int, sm_scale: float, Dv: int,
-          residual_ffn: bool, nthreads=None):
+          residual_ffn: bool, rows=None, nthreads=None, per_layer=False):
     """Layer stack of the inference loop in [ITO] § "Einfache Implementierung, enorme
     Effizienzgewinne" (the composition is a reading; see module docstring).
 
     layers[l] holds seeded inputs: q_i, k_i, w (indexer, with 'idx_dtypes'),
     q, kv (attention, bf16 bits) and W (FFN stand-in, bf16 bits [Dm, Dm]).
-    Per layer, with X kept in bf16 between steps:
-      route -> O = SparseMLA -> X1 = bf16(X + pad(sum_h O))
-            -> X = bf16(X1 W)          (plain linear map), or
-               X = bf16(X1 + X1 W)     (``residual_ffn``).
-    Returns (final X bf16 bits [L, Dm], list of per-layer T).
-    """
-    x = bf16_bits_to_f64(x0_bits)
-    L, Dm = x.shape
+    Per layer: route, then ``stack_layer``.  Per-layer inputs do not depend on
+    X, so rows are independent: with ``rows`` given, only those query rows are
+    computed; x0_bits and every layer's attention q then hold those rows only,
+    in the order of ``rows``, while the indexer inputs stay whole.
+    Returns (final X bf16 bits [n, Dm], list of per-layer T [1, L, k]) and,
+    with ``per_layer``, also the lists of X after every layer and of every
+    layer's attention output O (bf16 bits [n, Hq, Dv])."""
+    L = layers[0]["q_i"].shape[1]
     t_cache = np.full((1, L, topk_k), -1, dtype=np.int32)
-    ts = []
+    rows_a = None if rows is None else np.asarray(rows, dtype=np.int64)
+    x = np.asarray(x0_bits)
+    ts, xs, os_ = [], [], []
     for li, lay in enumerate(layers):
         def compute(lay=lay):
-            t, _ = indexer_topk(lay["q_i"], lay["k_i"], lay["w"], lay["idx_dtypes"], topk_k,
+            full = np.full((1, L, topk_k), -1, dtype=np.int32)
+            t, _ = indexer_topk(lay["q_i"], lay["k_i"], lay["w"], lay["idx_dtypes"], topk_k, rows=rows_a,
                                 nthreads=nthreads)
-            return t.reshape(1, L, topk_k)
+            full.reshape(L, topk_k)[slice(None) if rows_a is None else rows_a] = t
+            return full
 
         route(pattern, li, t_cache, compute)
         ts.append(t_cache.copy())
-        o_bits, _ = sparse_mla_dv(lay["q"], lay["kv"], t_cache, sm_scale, Dv, nthreads=nthreads)
-        o = bf16_bits_to_f64(o_bits).reshape(L, -1, Dv).sum(axis=1)
-        upd = np.zeros((L, Dm))
-        upd[:, :Dv] = o
-        x1 = bf16_bits_to_f64(f64_to_bf16_bits(x + upd))
-        y = x1 @ bf16_bits_to_f64(lay["W"])
-        x = bf16_bits_to_f64(f64_to_bf16_bits(x1 + y if residual_ffn else y))
-    return f64_to_bf16_bits(x), ts
+        x, o = stack_layer(x, t_cache, lay, sm_scale, Dv, residual_ffn, rows=rows_a, nthreads=nthreads)
+        xs.append(x)
+        os_.append(o)
+    return (x, ts, xs, os_) if per_layer else (x, ts)
 
 
 # ---------------------------------------------------------------- serving batches over paged caches

@@ -47,6 +47,7 @@ __device__ uint32_t block_select(Sh &sh, int n, int need, Get get, uint32_t *abo
     mn = 0xFFFFFFFFu; mx = 0u;
     for (int w = 0; w < NW; ++w) { mn = min(mn, sh.wtot[0][w]); mx = max(mx, sh.wtot[1][w]); }
     int top = (mn == mx) ? 0 : 32 - __builtin_clz(mn ^ mx);
+    const bool top_was_zero = top == 0;   // block-uniform: mn, mx come from the same LDS words
     uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
     uint32_t prefix = mn & pmask;
     uint32_t above_total = 0;
@@ -92,6 +93,10 @@ __device__ uint32_t block_select(Sh &sh, int n, int need, Get get, uint32_t *abo
         top = shift;
         __syncthreads();
     }
+    // Every caller writes sh.wtot next.  When all keys are equal the loop above
+    // never runs, so without this barrier a wavefront could overwrite a slot
+    // that a slower one is still reading in the min/max reduction.
+    if (top_was_zero) __syncthreads();
     *above_out = above_total;
     return prefix;
 }

@@ -105,3 +105,64 @@ def sample_rows(L: int, k: int, n_random: int, seed: int):
     fixed = {0, 1, min(L - 1, k - 1), min(L - 1, k), min(L - 1, k + 1), L // 2, L - 2 if L > 1 else 0, L - 1}
     rand = set(rng.choice(L, size=min(L, n_random), replace=False).tolist())
     return np.array(sorted(fixed | rand), dtype=np.int64)
+
+
+# ------------------------------------------------------------ stack X bounds
+
+U_F32 = 2.0 ** -24    # unit roundoff of fp32
+
+
+def _bf16_round(v):
+    """bf16 round-to-nearest-even of float64 values, by the oracle's pinned rounding."""
+    return oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(v))
+
+
+def _round_spread(v, d):
+    """max |R(a) - R(v)| over |a - v| <= d, R = bf16 rounding: R is monotone, so
+    the extremes are R(v - d) and R(v + d).  Zero wherever no rounding boundary
+    lies within d of v."""
+    r = _bf16_round(v)
+    return np.maximum(np.abs(_bf16_round(v + d) - r), np.abs(_bf16_round(v - d) - r))
+
+
+def stack_layer_bound(e_in, det, o_heads, x1_o, W, d_o, residual):
+    """Element-wise bound on |X_gpu - X_oracle| after one stack layer.
+
+    The layer computes X1 = bf16(X + pad(sum_h O)), then X = bf16(X1 W) or
+    bf16(X1 + X1 W); the GPU harness sums in fp32, the oracle in fp64, and both
+    round to bf16 at those two points.  Arguments:
+      e_in     bound on |X_gpu - X_oracle| entering the layer (0: same input),
+      det      the oracle's unrounded values at the two roundings
+               (stack_layer(..., detail=True)): pre_x1, pre_x,
+      o_heads  the oracle's attention output (float64 [n, Hq, Dv]),
+      x1_o     the oracle's X1 (= bf16(pre_x1)),
+      d_o      max |O_gpu - O_oracle| of this layer.
+    Each rounding is bounded by the spread of R over an interval around the
+    oracle's unrounded value (exact, see _round_spread):
+      d1 = e_in + Hq d_o + gamma_Hq sum_h |O_h| + u32 |pre_x1|   (O terms: first Dv columns)
+      e1 = spread(pre_x1, d1)
+      dY = (e1 + gamma_Dm (|X1| + e1)) |W|  [+ e1 + u32 |pre_x| when residual]
+      e  = spread(pre_x, dY).
+    """
+    n, Dm = det["pre_x1"].shape
+    Hq, Dv = o_heads.shape[1:]
+    d1 = np.array(e_in, dtype=np.float64) * np.ones((n, Dm))
+    d1[:, :Dv] += Hq * d_o + Hq * U_F32 * np.abs(o_heads).sum(axis=1)
+    d1 += U_F32 * np.abs(det["pre_x1"])          # the harness's fp32 add
+    e1 = _round_spread(det["pre_x1"], d1)
+    dy = (e1 + Dm * U_F32 * (np.abs(x1_o) + e1)) @ np.abs(W)
+    if residual:
+        dy = dy + e1 + U_F32 * np.abs(det["pre_x"])
+    return _round_spread(det["pre_x"], dy)
+
+
+def harness_layer(x, o, W, residual, torch):
+    """The GPU side of one stack layer's composition (harness arithmetic, not the
+    library): X1 = bf16(X + sum_h O) in fp32, then the FFN stand-in in fp32,
+    rounded once to bf16.  x bf16 [n, Dm], o bf16 [n, Hq, Dv], W bf16 [Dm, Dm]."""
+    Dv = o.shape[-1]
+    s = torch.zeros_like(x, dtype=torch.float32)
+    s[:, :Dv] = torch.sum(o, dim=1, dtype=torch.float32)
+    x1 = (x.float() + s).to(torch.bfloat16).float()
+    y = x1 @ W.float()
+    return ((x1 + y) if residual else y).to(torch.bfloat16)

@@ -265,3 +265,161 @@ def test_paged_mla_rejections():
     d = sa._PagedMlaDesc(2, 3, 10, 16, 8, 64, 576, 512, 64)
     assert L.sparse_mla_attn_paged_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
     assert n.value >= 3 * 8 + 3 * 64 * 4
+
+
+# ------------------------------------------------------------ binding checks
+#
+# The C ABI cannot see tensor sizes, so the binding checks every tensor against
+# the descriptor it builds before calling in.  Meta tensors (shape and dtype,
+# no storage) run these checks on the CPU; a call whose shapes are all right
+# goes on to the device check, which meta tensors fail with TypeError.
+
+import torch  # noqa: E402
+
+F8, B16, F32, I32 = torch.float8_e4m3fn, torch.bfloat16, torch.float32, torch.int32
+
+
+def m(*shape, dtype):
+    return torch.empty(*shape, dtype=dtype, device="meta")
+
+
+def idx_args(B=1, L=128, H=64, D=128):
+    return m(B, L, H, D, dtype=F8), m(B, L, D, dtype=F8), m(B, L, H, dtype=B16)
+
+
+@pytest.mark.parametrize("bad", ["k_batch", "k_dim", "k_dtype", "w_heads", "w_rows", "t_batch", "t_topk", "t_dtype",
+                                 "dbg_short", "dbg_dtype", "q_3d"])
+def test_binding_rejects_mismatched_indexer_tensors(bad):
+    q, k, w = idx_args()
+    kw = {}
+    if bad == "k_batch":
+        k = m(2, 128, 128, dtype=F8)
+    elif bad == "k_dim":
+        k = m(1, 128, 64, dtype=F8)
+    elif bad == "k_dtype":
+        k = m(1, 128, 128, dtype=B16)
+    elif bad == "w_heads":
+        w = m(1, 128, 32, dtype=B16)
+    elif bad == "w_rows":
+        w = m(1, 64, 64, dtype=B16)
+    elif bad == "t_batch":
+        kw["t_out"] = m(2, 128, 64, dtype=I32)
+    elif bad == "t_topk":
+        kw["t_out"] = m(1, 128, 32, dtype=I32)
+    elif bad == "t_dtype":
+        kw["t_out"] = m(1, 128, 64, dtype=torch.int64)
+    elif bad == "dbg_short":
+        kw["scores_dbg"] = m(1, 128, 100, dtype=F32)
+    elif bad == "dbg_dtype":
+        kw["scores_dbg"] = m(1, 128, 128, dtype=B16)
+    elif bad == "q_3d":
+        q = m(128, 64, 128, dtype=F8)
+    with pytest.raises(ValueError):
+        sa.idx_score_topk(q, k, w, 64, **kw)
+
+
+def test_binding_well_shaped_indexer_call_reaches_the_device_check():
+    q, k, w = idx_args()
+    with pytest.raises(TypeError):
+        sa.idx_score_topk(q, k, w, 64, t_out=m(1, 128, 64, dtype=I32), scores_dbg=m(1, 128, 128, dtype=F32))
+
+
+def test_binding_rejects_noncontiguous_tensors():
+    q, k, w = idx_args()
+    k_view = m(1, 128, 128, dtype=F8).transpose(1, 2)   # right shape, strided view
+    assert not k_view.is_contiguous()
+    with pytest.raises(ValueError):
+        sa.idx_score_topk(q, k_view, w, 64)
+
+
+def test_binding_router_checks_t_cache_against_the_indexer():
+    q, k, w = idx_args(B=2)
+    with pytest.raises(ValueError):
+        sa.idx_cache_route("FS", 0, q, k, w, m(1, 128, 64, dtype=I32))   # cache of a one-sequence batch
+    with pytest.raises(ValueError):
+        sa.idx_cache_route("FS", 0, q, k, w, m(2, 128, 64, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        sa.idx_cache_route("FS", 0, q, k, w, m(2, 128, 64, dtype=I32))
+
+
+@pytest.mark.parametrize("bad", ["scores_dtype", "pos_dtype", "pos_len", "t_shape"])
+def test_binding_rejects_mismatched_topk_tensors(bad):
+    s = m(8, 500, dtype=F32)
+    kw = {}
+    if bad == "scores_dtype":
+        s = m(8, 500, dtype=torch.float16)
+    elif bad == "pos_dtype":
+        kw["row_pos"] = m(8, dtype=torch.int64)
+    elif bad == "pos_len":
+        kw["row_pos"] = m(7, dtype=I32)
+    else:
+        kw["t_out"] = m(8, 16, dtype=I32)
+    with pytest.raises(ValueError):
+        sa.idx_topk(s, 32, **kw)
+
+
+@pytest.mark.parametrize("bad", ["q_dtype", "kv_dtype", "kv_dim", "kv_batch", "t_dtype", "t_rows", "out_dv",
+                                 "out_dtype", "lse_shape"])
+def test_binding_rejects_mismatched_mla_tensors(bad):
+    q, kv, t = m(2, 4, 128, 576, dtype=B16), m(2, 100, 576, dtype=B16), m(2, 4, 64, dtype=I32)
+    kw = {}
+    if bad == "q_dtype":
+        q = m(2, 4, 128, 576, dtype=F32)
+    elif bad == "kv_dtype":
+        kv = m(2, 100, 576, dtype=F8)
+    elif bad == "kv_dim":
+        kv = m(2, 100, 512, dtype=B16)
+    elif bad == "kv_batch":
+        kv = m(1, 100, 576, dtype=B16)
+    elif bad == "t_dtype":
+        t = m(2, 4, 64, dtype=torch.int64)
+    elif bad == "t_rows":
+        t = m(2, 3, 64, dtype=I32)
+    elif bad == "out_dv":
+        kw["out"] = m(2, 4, 128, 576, dtype=B16)
+    elif bad == "out_dtype":
+        kw["out"] = m(2, 4, 128, 512, dtype=F32)
+    else:
+        kw["lse"] = m(2, 4, 64, dtype=F32)
+    with pytest.raises(ValueError):
+        sa.sparse_mla_attn(q, kv, t, 0.04, 512, **kw)
+
+
+@pytest.mark.parametrize("bad", ["table_rows", "seq_lens_len", "qs_dtype", "k_dim", "w_rows", "t_rows"])
+def test_binding_rejects_mismatched_paged_indexer_tensors(bad):
+    q, kc, w = m(3, 64, 128, dtype=F8), m(40, 64, 128, dtype=F8), m(3, 64, dtype=B16)
+    table, qs, sl = m(2, 16, dtype=I32), m(3, dtype=I32), m(2, dtype=I32)
+    kw = {}
+    if bad == "table_rows":
+        table = m(3, 16, dtype=I32)
+    elif bad == "seq_lens_len":
+        sl = m(3, dtype=I32)
+    elif bad == "qs_dtype":
+        qs = m(3, dtype=torch.int64)
+    elif bad == "k_dim":
+        kc = m(40, 64, 64, dtype=F8)
+    elif bad == "w_rows":
+        w = m(2, 64, dtype=B16)
+    else:
+        kw["t_out"] = m(2, 64, dtype=I32)
+    with pytest.raises(ValueError):
+        sa.idx_score_topk_paged(q, kc, table, qs, sl, w, 64, 1000, **kw)
+
+
+@pytest.mark.parametrize("bad", ["kv_dim", "t_rows", "table_rows", "out_shape", "lse_shape"])
+def test_binding_rejects_mismatched_paged_mla_tensors(bad):
+    q, kvc, t = m(3, 128, 576, dtype=B16), m(40, 64, 576, dtype=B16), m(3, 64, dtype=I32)
+    table, qs, sl = m(2, 16, dtype=I32), m(3, dtype=I32), m(2, dtype=I32)
+    kw = {}
+    if bad == "kv_dim":
+        kvc = m(40, 64, 512, dtype=B16)
+    elif bad == "t_rows":
+        t = m(4, 64, dtype=I32)
+    elif bad == "table_rows":
+        table = m(1, 16, dtype=I32)
+    elif bad == "out_shape":
+        kw["out"] = m(3, 128, 576, dtype=B16)
+    else:
+        kw["lse"] = m(3, 64, dtype=F32)
+    with pytest.raises(ValueError):
+        sa.sparse_mla_attn_paged(q, kvc, table, qs, sl, t, 0.04, 512, **kw)

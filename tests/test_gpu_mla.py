@@ -36,7 +36,14 @@ def run_and_compare(B, Lq, Lk, Hq, Dqk, Dv, k, t_kind="random", seed=0):
                 t[b, i, :n] = rng.choice(Lk, size=n, replace=False)
             elif t_kind == "dup":
                 t[b, i] = rng.integers(0, min(Lk, k // 4 + 1), size=k)
+            elif t_kind == "beyond":
+                # valid rows mixed with indices at or past Lk, which select nothing
+                n = min(k, Lk) // 2
+                t[b, i, :n] = rng.choice(Lk, size=n, replace=False)
+                t[b, i, n:] = rng.choice([Lk, Lk + 1, Lk + 4093, 1 << 30, 2 ** 31 - 1], size=k - n)
+                rng.shuffle(t[b, i])
     tt = torch.from_numpy(t).to(DEV)
+    t = np.where(t >= Lk, -1, t)    # the oracle's form of the same index set
     scale = 1.0 / math.sqrt(Dqk)
     lse = torch.empty(B, Lq, Hq, dtype=torch.float32, device=DEV)
     out, _ = sa.sparse_mla_attn(q, kv, tt, scale, Dv, lse=lse)
@@ -95,3 +102,13 @@ def test_mla_wide_repeated_indices():
 
 def test_mla_wide_empty_index_set():
     run_and_compare(2, 2, 100, 64, 576, 512, 256, t_kind="empty")
+
+
+@pytest.mark.parametrize("B,Lq,Hq,Dqk,Dv,k", [
+    (2, 5, 8, 32, 32, 64),        # small latent kernel
+    (1, 3, 16, 576, 512, 200),    # 16-head latent kernel
+    (1, 3, 64, 576, 512, 1000),   # 64-head kernel, chunked + merge
+    (2, 40, 128, 576, 512, 96),   # 64-head kernel, one chunk per query
+])
+def test_indices_at_or_beyond_lk_are_skipped(B, Lq, Hq, Dqk, Dv, k):
+    run_and_compare(B, Lq, 700, Hq, Dqk, Dv, k, t_kind="beyond", seed=Hq + k)

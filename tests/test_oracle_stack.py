@@ -67,3 +67,35 @@ def test_shared_layer_result_differs_from_recomputing():
     for res in ("plain", "residual"):
         assert g["expected"][f"FS_{res}"] != g["expected"][f"FF_{res}"]
     assert g["expected"]["T0"] != g["expected"]["T1"]
+
+
+def _rand_bits(g, shape, std=1.0):
+    return (torch.randn(shape, generator=g) * std).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("residual", [False, True])
+def test_row_subset_equals_full_stack(residual):
+    """Per-layer inputs do not depend on X, so each row's path through the
+    stack is independent of the others: computing a subset of rows gives
+    exactly those rows of the full stack, for every layer's X and T."""
+    g = torch.Generator().manual_seed(5)
+    L, H, D, k, Hq, Dqk, Dv, Dm = 40, 4, 16, 6, 4, 24, 16, 24
+    layers = []
+    for _ in range(3):
+        layers.append(dict(q_i=_rand_bits(g, (1, L, H, D)), k_i=_rand_bits(g, (1, L, D)),
+                           w=torch.rand((1, L, H), generator=g).numpy(), idx_dtypes=("bf16", "bf16", "fp32"),
+                           q=_rand_bits(g, (1, L, Hq, Dqk)), kv=_rand_bits(g, (1, L, Dqk)),
+                           W=_rand_bits(g, (Dm, Dm), Dm ** -0.5)))
+    x0 = _rand_bits(g, (L, Dm))
+    xf, tf, xsf, osf = oracle.stack("FSF", x0, layers, k, Dqk ** -0.5, Dv, residual, per_layer=True)
+    rows = np.array([31, 0, 7, 39, 12])
+    sub = [dict(lay, q=np.ascontiguousarray(lay["q"][:, rows])) for lay in layers]
+    xr, tr, xsr, osr = oracle.stack("FSF", np.ascontiguousarray(x0[rows]), sub, k, Dqk ** -0.5, Dv, residual,
+                               rows=rows, per_layer=True)
+    assert np.array_equal(xr, xf[rows])
+    for a, b in zip(xsr, xsf):
+        assert np.array_equal(a, b[rows])
+    for a, b in zip(tr, tf):
+        assert np.array_equal(a[0, rows], b[0, rows])
+    for a, b in zip(osr, osf):
+        assert np.array_equal(a, b[rows])
