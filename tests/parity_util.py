@@ -136,7 +136,7 @@ def stack_layer_bound(e_in, det, o_heads, x1_o, W, d_o, residual):
                (stack_layer(..., detail=True)): pre_x1, pre_x,
       o_heads  the oracle's attention output (float64 [n, Hq, Dv]),
       x1_o     the oracle's X1 (= bf16(pre_x1)),
-      d_o      max |O_gpu - O_oracle| of this layer.
+      d_o      max |O_gpu - O_oracle| of this layer, a scalar or one value per row.
     Each rounding is bounded by the spread of R over an interval around the
     oracle's unrounded value (exact, see _round_spread):
       d1 = e_in + Hq d_o + gamma_Hq sum_h |O_h| + u32 |pre_x1|   (O terms: first Dv columns)
@@ -147,6 +147,7 @@ def stack_layer_bound(e_in, det, o_heads, x1_o, W, d_o, residual):
     n, Dm = det["pre_x1"].shape
     Hq, Dv = o_heads.shape[1:]
     d1 = np.array(e_in, dtype=np.float64) * np.ones((n, Dm))
+    d_o = np.broadcast_to(np.asarray(d_o, dtype=np.float64).reshape(-1, 1), (n, 1))
     d1[:, :Dv] += Hq * d_o + Hq * U_F32 * np.abs(o_heads).sum(axis=1)
     d1 += U_F32 * np.abs(det["pre_x1"])          # the harness's fp32 add
     e1 = _round_spread(det["pre_x1"], d1)

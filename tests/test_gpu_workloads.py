@@ -35,31 +35,49 @@ def _report(what, **vals):
                                            for k, v in vals.items()), flush=True)
 
 
+def _row_maxabs(a, b):
+    d = np.abs(_f64(a) - _f64(b))
+    return d.reshape(d.shape[0], -1).max(axis=1)
+
+
 def _check_stack(wl, pattern, rows, x0_rows, layers, t_gpu, xs_g, os_g, scale, residual):
     """Per layer: O against the oracle (given the GPU's T, and along the
     oracle's own chain), X after one layer from the GPU's input, and X along
     the chain, each element-wise.  rows: the query rows compared (their X and
-    O are in xs_g / os_g, in this order)."""
+    O are in xs_g / os_g, in this order; None: every row).
+
+    Along the chain the oracle uses its own index sets.  Where a row's T
+    differs from the GPU's (allowed at near-ties of the k-th score), its
+    attention output legitimately differs by more than the attention
+    tolerance, so that tolerance is asserted on the rows whose T agree; the X
+    bound uses every row's measured O difference and holds for all rows."""
     L, k = wl.Lq, wl.topk
+    rows_a = np.arange(L) if rows is None else np.asarray(rows)
     xo, ts_o, xs_o, os_o = oracle.stack(pattern, x0_rows, layers, k, scale, wl.Dv, residual, rows=rows,
                                         per_layer=True)
     e_chain = np.zeros(x0_rows.shape)
     x_in_g = x0_rows
-    worst = dict(step_x=0.0, chain_x=0.0, o_given_t=0.0, o_chain=0.0, x_rel_chain=0.0)
+    worst = dict(step_x=0.0, chain_x=0.0, o_given_t=0.0, o_chain_same_t=0.0, o_chain_other_t=0.0,
+                 rows_t_differ=0, x_rel_chain=0.0)
     for l in range(len(pattern)):
         W = _f64(layers[l]["W"])
         # one layer from the GPU's own input X and index set
         x_st, o_st, det = oracle.stack_layer(x_in_g, t_gpu[l], layers[l], scale, wl.Dv, residual, rows=rows,
                                              detail=True)
-        d_o = float(np.abs(_f64(os_g[l]) - _f64(o_st)).max())
-        assert d_o <= ATT_TOL, f"layer {l}: attention given the GPU's T, max-abs {d_o}"
+        d_o = _row_maxabs(os_g[l], o_st)
+        assert d_o.max() <= ATT_TOL, f"layer {l}: attention given the GPU's T, max-abs {d_o.max()}"
         e = stack_layer_bound(0.0, det, _f64(o_st), _f64(oracle.f64_to_bf16_bits(det["pre_x1"])), W, d_o,
                               residual)
         err = np.abs(_f64(xs_g[l]) - _f64(x_st))
         assert np.all(err <= e), f"layer {l}: X from the same input off by {err.max()} (bound {e[err > e][:3]})"
         # the same layer along the oracle's chain from X0
-        d_oc = float(np.abs(_f64(os_g[l]) - _f64(os_o[l])).max())
-        assert d_oc <= ATT_TOL, f"layer {l}: attention along the chain, max-abs {d_oc}"
+        same_t = np.all(ts_o[l][0, rows_a] == t_gpu[l][0, rows_a], axis=1)
+        d_oc = _row_maxabs(os_g[l], os_o[l])
+        if same_t.any():
+            assert d_oc[same_t].max() <= ATT_TOL, f"layer {l}: attention along the chain, max-abs {d_oc.max()}"
+        worst["o_chain_same_t"] = max(worst["o_chain_same_t"], float(d_oc[same_t].max(initial=0.0)))
+        worst["o_chain_other_t"] = max(worst["o_chain_other_t"], float(d_oc[~same_t].max(initial=0.0)))
+        worst["rows_t_differ"] = max(worst["rows_t_differ"], int((~same_t).sum()))
         x_prev_o = x0_rows if l == 0 else xs_o[l - 1]
         _, _, det_c = oracle.stack_layer(x_prev_o, ts_o[l], layers[l], scale, wl.Dv, residual, rows=rows,
                                          detail=True)
@@ -69,8 +87,7 @@ def _check_stack(wl, pattern, rows, x0_rows, layers, t_gpu, xs_g, os_g, scale, r
         assert np.all(err_c <= e_chain), f"layer {l}: X along the chain off by {err_c.max()}"
         worst["step_x"] = max(worst["step_x"], float(err.max()))
         worst["chain_x"] = max(worst["chain_x"], float(err_c.max()))
-        worst["o_given_t"] = max(worst["o_given_t"], d_o)
-        worst["o_chain"] = max(worst["o_chain"], d_oc)
+        worst["o_given_t"] = max(worst["o_given_t"], float(d_o.max()))
         x_in_g = xs_g[l]
     xr = _f64(xo)
     worst["x_rel_chain"] = float(np.linalg.norm(_f64(xs_g[-1]) - xr) / np.linalg.norm(xr))
@@ -116,13 +133,13 @@ def test_tiny_stack_full():
 def test_prefill_8k_sampled():
     wl = inputs.WORKLOADS["prefill_8k"]
     q, k, w = inputs.indexer_inputs(wl, 0, DEV)
-    scores = torch.empty(wl.Lq, wl.Lk, dtype=torch.float32, device=DEV)
+    scores = torch.empty(wl.B, wl.Lq, wl.Lk, dtype=torch.float32, device=DEV)
     t = sa.idx_score_topk(q, k, w, wl.topk, scores_dbg=scores)
     torch.cuda.synchronize()
     check_t_invariants_gpu(t, wl.Lq, wl.Lk, wl.topk)
     rows = sample_rows(wl.Lq, wl.topk, 128, seed=1001)
     to, so = indexer_oracle(q, k, w, wl.topk, rows=rows)
-    sg = scores.cpu().numpy()[rows]
+    sg = scores.cpu().numpy()[0][rows]
     check_scores(sg, so, RTOL["fp8"], "prefill_8k")
     pos = oracle.row_positions(1, wl.Lq, wl.Lk, rows)
     ov = check_index_sets(t.cpu().numpy()[0][rows], to, so, pos, wl.topk, RTOL["fp8"], "prefill_8k")
@@ -271,5 +288,4 @@ def test_stack_32k_fsss_group_sampled():
         del qa, kv, o, W
     torch.cuda.empty_cache()
     ts_o, worst = _check_stack(wl, pattern, rows, x0_rows, layers, t_gpu, xs_g, os_g, scale, True)
-    same_t = sum(np.array_equal(ts_o[0][0, r], t_gpu[0][0, r]) for r in rows)
-    _report("stack_32k FSSS", rows=len(rows), overlap=ov, rows_t_identical=same_t, **worst)
+    _report("stack_32k FSSS", rows=len(rows), overlap=ov, **worst)
