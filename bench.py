@@ -49,8 +49,11 @@ def parse():
     ap.add_argument("--profile", choices=["prefill", "decode", "mla_prefill", "copy"],
                     help="run warmup+steps of one workload (for profiler runs) and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
-                    help="write the headline kernel's HBM traffic from rocprofv3 counter runs in DIR "
-                         "(subdirectories fetch/, write/, copy_fetch/, copy_write/) and exit")
+                    help="HBM traffic per launch from rocprofv3 counter runs in DIR (subdirectories fetch/, "
+                         "write/, copy_fetch/, copy_write/), scaled by the copy calibration; prints it and, for "
+                         "the headline kernel, records it under profiles/; then exits")
+    ap.add_argument("--kernels", default="prefill_kernel",
+                    help="with --traffic-from: comma-separated kernel-name parts to report")
     return ap.parse_args()
 
 
@@ -97,18 +100,22 @@ def decode(args, torch, sa, inputs):
     t = torch.empty(wl.B, wl.Lq, wl.topk, dtype=torch.int32, device=dev)
     out = torch.empty(wl.B, wl.Lq, wl.Hq, wl.Dv, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(sa.idx_score_topk_workspace(q, k, w, wl.topk), dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)   # evicts the 256 MB MALL
+    # Cold timing: a read-only pass over 512 MB (twice the 256 MB MALL) before
+    # each timed call evicts the caches.  It only reads, so the timed call
+    # inherits no dirty lines to write back.
+    flush = torch.ones(128 << 20, dtype=torch.int32, device=dev)
     scale = 1.0 / math.sqrt(wl.Dqk)
     sa.idx_cache_route("FSSS", 0, q, k, w, t, ws=ws)
     torch.cuda.synchronize()
     n = max(3, args.steps)
 
-    def timed(fn):
+    def timed(fn, cold=True):
         for _ in range(2):
             fn()
         tot = 0.0
         for _ in range(n):
-            flush.zero_()
+            if cold:
+                torch.sum(flush)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
@@ -117,8 +124,12 @@ def decode(args, torch, sa, inputs):
             tot += e0.elapsed_time(e1)
         return tot / n
 
-    t_idx = timed(lambda: sa.idx_cache_route("FSSS", 0, q, k, w, t, ws=ws))
-    t_att = timed(lambda: sa.sparse_mla_attn(qa, kv, t, scale, wl.Dv, out=out))
+    f_idx = lambda: sa.idx_cache_route("FSSS", 0, q, k, w, t, ws=ws)   # noqa: E731
+    f_att = lambda: sa.sparse_mla_attn(qa, kv, t, scale, wl.Dv, out=out)   # noqa: E731
+    t_idx = timed(f_idx)
+    t_att = timed(f_att)
+    t_idx_warm = timed(f_idx, cold=False)
+    t_att_warm = timed(f_att, cold=False)
     t_f = t_idx + t_att
 
     # the same step as a serving batch: caches in pools of 64-row pages at
@@ -149,9 +160,17 @@ def decode(args, torch, sa, inputs):
     gathered = wl.B * wl.Lq * wl.topk * wl.Dqk * 2
     key_bytes = wl.B * wl.Lk * wl.D
     tok = wl.B * wl.Lq
+    layer_bytes = decode_layer_bytes(wl)
     return {
         "workload": "decode_200k", "batch": wl.B, "context": wl.Lk,
         "indexer_topk_ms": round(t_idx, 4), "sparse_mla_ms": round(t_att, 4),
+        "indexer_topk_ms_warm": round(t_idx_warm, 4), "sparse_mla_ms_warm": round(t_att_warm, 4),
+        "full_layer_roofline": {
+            "bound": "hbm", "algorithmic_bytes": layer_bytes, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "achieved": round(layer_bytes / (t_f * 1e-3) / 1e9, 1),
+            "frac": round(layer_bytes / (t_f * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "ideal_ms": round(layer_bytes / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
+            "bytes": "keys + gathered latent rows + q, w, Q, O and T (score rows in the workspace excluded)"},
         "full_layer_tok_s": round(tok / (t_f * 1e-3), 1),
         "shared_layer_tok_s": round(tok / (t_att * 1e-3), 1),
         "group_FSSS_tok_s": round(tok / ((t_f + 3 * t_att) * 1e-3), 1),
@@ -159,7 +178,7 @@ def decode(args, torch, sa, inputs):
         "indexer_key_read_GBs": round(key_bytes / (t_idx * 1e-3) / 1e9, 1),
         "gather_GBs": round(gathered / (t_att * 1e-3) / 1e9, 1),
         "gather_frac_hbm": round(gathered / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "note": "caches flushed before each timed call; one layer = one call each",
+        "note": "cold: a read-only pass over 512 MB before each timed call; warm: back to back; one layer = one call each",
         "serving_paged": {
             "block_size": bs, "pages": "random slots of one pool, shared block table",
             "indexer_topk_ms": round(t_pidx, 4), "sparse_mla_ms": round(t_patt, 4),
@@ -169,34 +188,39 @@ def decode(args, torch, sa, inputs):
     }
 
 
+def decode_layer_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one Full decode layer: every key of every
+    sequence once, the selected latent rows once, the indexer queries and
+    weights, the attention queries and outputs, and T."""
+    keys = wl.B * wl.Lk * wl.D                       # fp8
+    gathered = wl.B * wl.Lq * wl.topk * wl.Dqk * 2   # bf16 latent rows
+    q_i = wl.B * wl.Lq * wl.H * wl.D + wl.B * wl.Lq * wl.H * 2
+    q_a = wl.B * wl.Lq * wl.Hq * wl.Dqk * 2
+    o = wl.B * wl.Lq * wl.Hq * wl.Dv * 2
+    t = wl.B * wl.Lq * wl.topk * 4
+    return keys + gathered + q_i + q_a + o + t
+
+
 COPY_BYTES = 1 << 30   # the calibration copy moves this many bytes each way
 
 
 def retention_sweep(args, torch, sa, inputs):
     """Layer patterns keeping 1/1, 1/2, 1/4 and 1/8 of the 16 layers Full, at the
-    32K-token stack shape: per-layer times of the indexer (Full layers only),
-    sparse MLA and the FFN stand-in, the stack time they imply for each pattern,
-    and one directly timed F,S,S,S x 4 stack for comparison."""
+    32K-token stack shape, each timed end to end: the stack runs all 16 layers
+    with X chained through attention and the FFN stand-in (residual), layer l
+    taking input set l mod 4 (four seeded sets of indexer, attention and FFN
+    inputs).  Next to each measured time, the model that adds per-layer times
+    (Full layers x indexer + all layers x (attention + FFN))."""
+    from sparse_attention_indexer_lightning_amd.stack import Stack, compose, layer_inputs
     wl = inputs.WORKLOADS["stack_32k"]
     dev = torch.device("cuda:0")
-    L, n_layers = wl.Lq, wl.layers
-    q, k, w = inputs.indexer_inputs(wl, 0, dev)
-    qa, kv = inputs.attention_inputs(wl, 0, dev)
-    W = inputs.ffn_weight(wl, 0, dev)
-    x = inputs.stack_x0(wl, dev)
-    t_cache = torch.empty(wl.B, L, wl.topk, dtype=torch.int32, device=dev)
-    out = torch.empty(wl.B, L, wl.Hq, wl.Dv, dtype=torch.bfloat16, device=dev)
+    n_layers, n_sets = wl.layers, 4
+    sets = [layer_inputs(wl, i, dev) for i in range(n_sets)]
+    x0 = inputs.stack_x0(wl, dev)
+    st = Stack(wl, [sets[l % n_sets] for l in range(n_layers)], x0, residual=True)
     scale = 1.0 / math.sqrt(wl.Dqk)
-    sa.idx_cache_route("F", 0, q, k, w, t_cache)
 
-    def layer(pattern, i):
-        sa.idx_cache_route(pattern, i, q, k, w, t_cache)
-        sa.sparse_mla_attn(qa, kv, t_cache, scale, wl.Dv, out=out)
-        x1 = x.clone()
-        x1[:, :wl.Dv] += out[0].sum(dim=1)
-        return x1 + x1 @ W
-
-    def timed(fn, n=3):
+    def timed(fn, n=2):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -207,25 +231,30 @@ def retention_sweep(args, torch, sa, inputs):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    t_idx = timed(lambda: sa.idx_cache_route("F", 0, q, k, w, t_cache))
-    t_att = timed(lambda: sa.sparse_mla_attn(qa, kv, t_cache, scale, wl.Dv, out=out))
-    t_ffn = timed(lambda: layer("FS", 1)) - t_att   # head sum, residual and FFN GEMM
+    s0 = sets[0]
+    t_idx = timed(lambda: sa.idx_cache_route("F", 0, s0["q_i"], s0["k_i"], s0["w"], st.t_cache, ws=st.ws), 3)
+    t_att = timed(lambda: sa.sparse_mla_attn(s0["q"], s0["kv"], st.t_cache, scale, wl.Dv, out=st.out), 3)
+    t_ffn = timed(lambda: compose(x0, st.out[0], s0["W"], True, False), 3)
     pats = {"1/1": "F" * n_layers, "1/2": "FS" * (n_layers // 2), "1/4": "FSSS" * (n_layers // 4),
             "1/8": "FSSSSSSS" * (n_layers // 8)}
     res = {}
-    full = n_layers * (t_idx + t_att + t_ffn)
     for name, pat in pats.items():
         nf = pat.count("F")
-        stack = nf * t_idx + n_layers * (t_att + t_ffn)
-        res[name] = {"pattern": pat, "full_layers": nf, "indexer_ms": round(nf * t_idx, 3),
-                     "indexer_saved_ms": round((n_layers - nf) * t_idx, 3), "stack_ms": round(stack, 3),
-                     "speedup_vs_all_full": round(full / stack, 4)}
-    measured = timed(lambda: [layer(pats["1/4"], i) for i in range(n_layers)], n=1)
-    del q, k, w, qa, kv, out, W, x, t_cache
-    return {"workload": "stack_32k", "L": L, "layers": n_layers, "indexer_ms_per_full_layer": round(t_idx, 3),
-            "sparse_mla_ms_per_layer": round(t_att, 3), "ffn_and_residual_ms_per_layer": round(t_ffn, 3),
-            "patterns": res, "measured_FSSSx4_stack_ms": round(measured, 3),
-            "note": "stack_ms = Full layers x indexer + all layers x (sparse MLA + FFN stand-in)"}
+        res[name] = {"pattern": pat, "full_layers": nf,
+                     "stack_ms": round(timed(lambda: st.run(pat)), 3),
+                     "modelled_stack_ms": round(nf * t_idx + n_layers * (t_att + t_ffn), 3),
+                     "indexer_ms": round(nf * t_idx, 3), "indexer_saved_ms": round((n_layers - nf) * t_idx, 3)}
+    full = res["1/1"]["stack_ms"]
+    for r in res.values():
+        r["speedup_vs_all_full"] = round(full / r["stack_ms"], 4)
+        r["measured_saving_ms"] = round(full - r["stack_ms"], 3)
+    del sets, st
+    torch.cuda.empty_cache()
+    return {"workload": "stack_32k", "L": wl.Lq, "layers": n_layers, "input_sets": n_sets,
+            "indexer_ms_per_full_layer": round(t_idx, 3), "sparse_mla_ms_per_layer": round(t_att, 3),
+            "ffn_and_residual_ms_per_layer": round(t_ffn, 3), "patterns": res,
+            "note": "stack_ms: the whole 16-layer stack timed end to end (X chained, layer l on input set l mod 4); "
+                    "modelled_stack_ms = Full layers x indexer + all layers x (sparse MLA + FFN stand-in)"}
 
 
 def profile_run(args, torch, sa, inputs):
@@ -279,32 +308,50 @@ def _counter_kb(run_dir, counter, name_part):
 
 
 def traffic_from(args):
-    """Scales the headline kernel's FETCH_SIZE / WRITE_SIZE by what the same
-    counters read for a copy of COPY_BYTES, and records the result."""
+    """Scales each kernel's FETCH_SIZE / WRITE_SIZE by what the same counters
+    read for a device copy of COPY_BYTES each way, and prints the bytes per
+    launch; the headline kernel's figure is also recorded in TRAFFIC_FILE."""
     d = args.traffic_from
-    kname = "prefill_kernel"
     copy_name = "copyBuffer"   # the device-to-device copy torch issues for dst.copy_(src)
-    fetch_kb = _counter_kb(os.path.join(d, "fetch"), "FETCH_SIZE", kname)
-    write_kb = _counter_kb(os.path.join(d, "write"), "WRITE_SIZE", kname)
     cf_kb = _counter_kb(os.path.join(d, "copy_fetch"), "FETCH_SIZE", copy_name)
     cw_kb = _counter_kb(os.path.join(d, "copy_write"), "WRITE_SIZE", copy_name)
     f_fetch = cf_kb * 1024.0 / COPY_BYTES
     f_write = cw_kb * 1024.0 / COPY_BYTES
-    read_b = fetch_kb * 1024.0 / f_fetch
-    write_b = write_kb * 1024.0 / f_write
-    rec = {"kernel": kname, "workload": "prefill_64k", "kernel_source_sha": _kernel_sha(),
-           "fetch_size_kb": fetch_kb, "write_size_kb": write_kb,
-           "copy_bytes_each_way": COPY_BYTES, "copy_fetch_kb": cf_kb, "copy_write_kb": cw_kb,
-           "scale_fetch": f_fetch, "scale_write": f_write,
-           "read_bytes_per_launch": read_b, "write_bytes_per_launch": write_b,
-           "bytes_per_launch": read_b + write_b}
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
-    print(json.dumps(rec))
+    out = []
+    for kname in [x for x in args.kernels.split(",") if x]:
+        fetch_kb = _counter_kb(os.path.join(d, "fetch"), "FETCH_SIZE", kname)
+        write_kb = _counter_kb(os.path.join(d, "write"), "WRITE_SIZE", kname)
+        read_b = fetch_kb * 1024.0 / f_fetch
+        write_b = write_kb * 1024.0 / f_write
+        rec = {"kernel": kname, "kernel_source_sha": _kernel_sha(),
+               "fetch_size_kb": fetch_kb, "write_size_kb": write_kb,
+               "copy_bytes_each_way": COPY_BYTES, "copy_fetch_kb": cf_kb, "copy_write_kb": cw_kb,
+               "scale_fetch": f_fetch, "scale_write": f_write,
+               "read_bytes_per_launch": read_b, "write_bytes_per_launch": write_b,
+               "bytes_per_launch": read_b + write_b}
+        if kname == "prefill_kernel":
+            rec["workload"] = "prefill_64k"
+            with open(TRAFFIC_FILE, "w") as f:
+                json.dump(rec, f, indent=1)
+        out.append(rec)
+    print(json.dumps(out))
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(args, inputs, torch):
-    """Oracle rows/s on the host, scaled to pairs/s (bounded seeded row sample)."""
+    """Oracle pairs/s on the host (bounded seeded row sample of prefill_64k):
+    once on the CPU share this process is given (OMP_NUM_THREADS, else every
+    core), once on one thread."""
     import numpy as np
 
     import oracle
@@ -314,21 +361,32 @@ def cpu_baseline(args, inputs, torch):
     kr = k.cpu().view(torch.uint8).numpy()
     wr = w.cpu().view(torch.int16).numpy()
     del q, k, w
-    threads = oracle.default_threads()
+    host_cores = os.cpu_count() or 1
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or host_cores
+    threads = max(1, min(host_cores, share))
     rng = np.random.default_rng(2024)
     order = rng.permutation(wl.Lq)
-    done_rows, done_pairs, wall = 0, 0, 0.0
-    batch = 2 * threads
-    while wall < args.cpu_seconds and done_rows < wl.Lq:
-        rows = np.sort(order[done_rows:done_rows + batch]).astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.indexer_topk(qr, kr, wr, ("fp8", "fp8", "bf16"), wl.topk, rows=rows, nthreads=threads)
-        wall += time.perf_counter() - t0
-        done_rows += rows.size
-        done_pairs += int((rows + 1).sum())
-    return {"value": round(done_pairs / wall, 1), "unit": "pairs/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done_rows} seeded random query rows of prefill_64k ({done_pairs} causal pairs, "
-                      f"fp64 scores + top-k), {wall:.1f} s wall"}
+
+    def run(nthreads, seconds, start):
+        done_rows, done_pairs, wall = 0, 0, 0.0
+        batch = 2 * nthreads
+        while wall < seconds and start + done_rows < wl.Lq:
+            rows = np.sort(order[start + done_rows:start + done_rows + batch]).astype(np.int64)
+            t0 = time.perf_counter()
+            oracle.indexer_topk(qr, kr, wr, ("fp8", "fp8", "bf16"), wl.topk, rows=rows, nthreads=nthreads)
+            wall += time.perf_counter() - t0
+            done_rows += rows.size
+            done_pairs += int((rows + 1).sum())
+        return done_rows, done_pairs, wall
+
+    rows_n, pairs_n, wall_n = run(threads, args.cpu_seconds, 0)
+    rows_1, pairs_1, wall_1 = run(1, args.cpu_seconds / 3, rows_n)
+    return {"value": round(pairs_n / wall_n, 1), "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_n} seeded random query rows of prefill_64k ({pairs_n} causal pairs, fp64 scores + "
+                      f"top-k), {wall_n:.1f} s wall on {threads} threads",
+            "host_cpu": _cpu_model(), "host_logical_cores": host_cores,
+            "one_thread": {"value": round(pairs_1 / wall_1, 1), "unit": "pairs/s",
+                           "sample": f"{rows_1} further rows of the same order ({pairs_1} pairs), {wall_1:.1f} s"}}
 
 
 def main():
@@ -387,7 +445,7 @@ def main():
 def _kernel_sha() -> str:
     import hashlib
     h = hashlib.sha256()
-    for n in ("indexer.hip", "device_common.h"):
+    for n in ("indexer.hip", "device_common.h", "select_common.h", "kernels.h"):
         with open(os.path.join(ROOT, "sparse_attention_indexer_lightning_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -42,3 +42,25 @@ def greedy_pattern(n_layers: int, loss_fn: Callable[[str], float], n_full: int =
         pattern = list(best[0])
         path.append(best)
     return path
+
+
+def stack_deviation_loss(stack):
+    """Loss for ``greedy_pattern`` from a layer stack run through the library
+    (``stack.Stack``): the relative deviation of a pattern's final X from the
+    all-Full stack's final X.  Without calibration data or trained weights this
+    is the one loss the synthetic stack offers: how much the model's output
+    moves when layers reuse the cached index set.  Evaluations are memoised per
+    pattern."""
+    from .stack import relative_deviation
+
+    n = len(stack.layers)
+    ref = stack.run("F" * n).clone()
+    memo = {}
+
+    def loss(pattern: str) -> float:
+        if pattern not in memo:
+            memo[pattern] = relative_deviation(stack.run(pattern), ref)
+        return memo[pattern]
+
+    loss.memo = memo
+    return loss

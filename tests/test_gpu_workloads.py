@@ -85,6 +85,11 @@ def _check_stack(wl, pattern, rows, x0_rows, layers, t_gpu, xs_g, os_g, scale, r
                                     _f64(oracle.f64_to_bf16_bits(det_c["pre_x1"])), W, d_oc, residual)
         err_c = np.abs(_f64(xs_g[l]) - _f64(xs_o[l]))
         assert np.all(err_c <= e_chain), f"layer {l}: X along the chain off by {err_c.max()}"
+        if float(err.max()) > worst["step_x"]:
+            i = np.unravel_index(np.argmax(err), err.shape)
+            worst["step_x_at_abs_x"] = float(abs(_f64(x_st)[i]))
+            worst["step_x_bound_there"] = float(e[i])
+        worst["x_abs_max"] = max(worst.get("x_abs_max", 0.0), float(np.abs(_f64(x_st)).max()))
         worst["step_x"] = max(worst["step_x"], float(err.max()))
         worst["chain_x"] = max(worst["chain_x"], float(err_c.max()))
         worst["o_given_t"] = max(worst["o_given_t"], float(d_o.max()))
