@@ -110,12 +110,23 @@ def decode(args, torch, sa, inputs):
     n = max(3, args.steps)
 
     def timed(fn, cold=True):
+        """ms per call.  cold: each call alone after the flush (the flush kernel
+        also covers the host's launch latency).  warm: n calls back to back
+        between one pair of events."""
         for _ in range(2):
             fn()
+        torch.cuda.synchronize()
+        if not cold:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
         tot = 0.0
         for _ in range(n):
-            if cold:
-                torch.sum(flush)
+            torch.sum(flush)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
