@@ -58,10 +58,11 @@ _lib = None
 
 
 def lib():
-    """Load the in-tree libidxcache.so (raises if it has not been built)."""
+    """Load the in-tree libidxcache.so (raises if it has not been built).
+    IDXCACHE_LIB names another build of the same library to load instead."""
     global _lib
     if _lib is None:
-        path = _build.LIB_PATH
+        path = os.environ.get("IDXCACHE_LIB") or _build.LIB_PATH
         if not os.path.exists(path):
             raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
                               "or python -m sparse_attention_indexer_lightning_amd._build")

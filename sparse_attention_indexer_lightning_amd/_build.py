@@ -24,8 +24,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
 SOURCE_FLAGS = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
-def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _compile(src: str, obj: str, defines=()) -> None:
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *[f"-D{d}" for d in defines], "-c", src,
+           "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,28 +34,30 @@ def _compile(src: str, obj: str) -> None:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library in-tree."""
-    os.makedirs(LIB_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB_PATH, defines=()) -> str:
+    """Compile every HIP source and link the shared library (in-tree by
+    default; ``out`` and ``defines`` serve other builds of the same sources)."""
+    obj_dir = os.path.dirname(out) if out == LIB_PATH else out + ".objs"
+    os.makedirs(obj_dir, exist_ok=True)
     objs = []
     jobs = []
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         for s in SOURCES:
             src = os.path.join(CSRC, s)
-            obj = os.path.join(LIB_DIR, s + ".o")
+            obj = os.path.join(obj_dir, s + ".o")
             objs.append(obj)
-            jobs.append(ex.submit(_compile, src, obj))
+            jobs.append(ex.submit(_compile, src, obj, tuple(defines)))
         for j in jobs:
             j.result()
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

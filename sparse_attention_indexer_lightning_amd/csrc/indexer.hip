@@ -897,7 +897,11 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         const int krow = tid / CPK, kcol = (tid % CPK) * 16;
         auto fetch1 = [&](int blk) {
             const int key = min(blk * KB + krow, p.Lk - 1);   // past Lk: clamped, never used
-            return *reinterpret_cast<const v4i *>(kseq + (size_t)key * S::ROWB + kcol);
+            // 32-bit offset from the sequence's base (this sweep runs with 16-bit
+            // key indices, so at most 65536 keys of 128 bytes):
+            // one VALU add instead of 64-bit address arithmetic per staging load
+            const uint32_t off = (uint32_t)key * (uint32_t)S::ROWB + (uint32_t)kcol;
+            return *reinterpret_cast<const v4i *>(kseq + off);
         };
         auto stash1 = [&](int buf, const v4i &v) {
             *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + krow * S::PITCH + kcol) = v;
