@@ -50,7 +50,9 @@ typedef enum {
     IDXC_ERR_UNSUPPORTED = -5, /* valid request this build has no kernel for */
     IDXC_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required */
     IDXC_ERR_PATTERN = -7,     /* layer pattern invalid (see idx_cache_route) */
-    IDXC_ERR_HIP = -8          /* the HIP runtime reported an error at launch */
+    IDXC_ERR_HIP = -8,         /* the HIP runtime reported an error at launch */
+    IDXC_ERR_SCRATCH = -9      /* idx_score_topk_noalloc: the request needs more than
+                                  the library's static scratch (128 MiB per GPU) */
 } idxc_status;
 
 typedef enum {
@@ -99,6 +101,24 @@ idxc_status idx_score_topk_workspace(const idxc_indexer_desc *desc, size_t *byte
 idxc_status idx_score_topk(const idxc_indexer_desc *desc, const void *q, const void *k,
                            const void *w, int32_t *t_out, float *scores_dbg, void *ws,
                            size_t ws_bytes, void *stream);
+
+/*
+ * idx_score_topk without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, hosts that forbid allocation during a step.
+ * Same descriptor, tensors, result and checks as idx_score_topk (no scores_dbg).
+ * Where idx_score_topk would need a workspace, this call uses a static device
+ * array of the library instead: 128 MiB per GPU, reserved when the library's
+ * code object is loaded on that GPU and held until the process ends (its
+ * address is looked up once per device, on the first call there).  A request
+ * whose idx_score_topk_workspace() exceeds 128 MiB returns IDXC_ERR_SCRATCH
+ * and enqueues nothing (the decode step of 32 sequences of 200,000 keys needs
+ * about 77 MB: the score rows and the top-k's candidate regions).  All calls
+ * on one GPU share the array: calls that may overlap on one GPU (different
+ * streams without ordering) race and must not be issued.
+ */
+idxc_status idx_score_topk_noalloc(const idxc_indexer_desc *desc, const void *q, const void *k,
+                                   const void *w, int32_t *t_out, void *stream);
 
 /* Workspace bytes for idx_topk (may be 0: it is nonzero when few long rows
  * are each split over several workgroups). */

@@ -21,11 +21,12 @@ __all__ = [
     "STATUS", "DTYPE", "idx_overlap", "overlap_matrix",
     "idx_score_topk_paged", "idx_score_topk_paged_workspace", "idx_cache_route_paged",
     "sparse_mla_attn_paged", "sparse_mla_attn_paged_workspace", "paged_indexer_desc", "paged_mla_desc",
+    "idx_score_topk_noalloc",
 ]
 
 STATUS = {0: "IDXC_OK", -1: "IDXC_ERR_NULL", -2: "IDXC_ERR_SHAPE", -3: "IDXC_ERR_DTYPE",
           -4: "IDXC_ERR_ALIGN", -5: "IDXC_ERR_UNSUPPORTED", -6: "IDXC_ERR_WORKSPACE",
-          -7: "IDXC_ERR_PATTERN", -8: "IDXC_ERR_HIP"}
+          -7: "IDXC_ERR_PATTERN", -8: "IDXC_ERR_HIP", -9: "IDXC_ERR_SCRATCH"}
 DTYPE = {torch.bfloat16: 1, torch.float8_e4m3fn: 2, torch.float32: 3}
 
 
@@ -80,6 +81,8 @@ def lib():
         L.idx_score_topk_workspace.argtypes = [dp, szp]
         L.idx_score_topk.restype = i32
         L.idx_score_topk.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.idx_score_topk_noalloc.restype = i32
+        L.idx_score_topk_noalloc.argtypes = [dp, vp, vp, vp, vp, vp]
         L.idx_topk_workspace.restype = i32
         L.idx_topk_workspace.argtypes = [i32, i32, i32, szp]
         L.idx_topk.restype = i32
@@ -233,6 +236,21 @@ def idx_score_topk(q, k, w, topk: int, t_out=None, scores_dbg=None, ws=None, str
     _check(lib().idx_score_topk(ctypes.byref(d), _p(q), _p(k), _p(w), _p(t_out), _p(scores_dbg), _p(ws), wsb,
                                 _stream(stream, q.device)), "idx_score_topk")
     _keep_alive(stream, *mine)
+    return t_out
+
+
+def idx_score_topk_noalloc(q, k, w, topk: int, t_out, stream=None):
+    """idx_score_topk for callers that cannot allocate (graph capture, serving
+    loops): the library's static device scratch replaces the workspace, and
+    nothing is allocated here either, so the caller passes T.  Calls that may
+    overlap on one GPU share that scratch and must not be issued."""
+    if t_out is None:
+        raise ValueError("t_out is required: this call allocates nothing")
+    _check_indexer(q, k, w, topk, t_out, "t_out")
+    _same_device(("q", q), ("k", k), ("w", w), ("t_out", t_out))
+    d = indexer_desc(q, k, w, topk)
+    _check(lib().idx_score_topk_noalloc(ctypes.byref(d), _p(q), _p(k), _p(w), _p(t_out), _stream(stream, q.device)),
+           "idx_score_topk_noalloc")
     return t_out
 
 

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/idxcache.h"
 #include "kernels.h"
 
@@ -80,10 +82,9 @@ size_t decode_ws_bytes(const idxc_indexer_desc *d) {
 
 idxc_status from_hip(hipError_t e) { return e == hipSuccess ? IDXC_OK : IDXC_ERR_HIP; }
 
-// Validation of the tensors of an F-layer call; shared by score_topk and route.
-idxc_status check_indexer_call(const idxc_indexer_desc *d, const void *q, const void *k, const void *w,
-                               const int32_t *t, const float *scores_dbg, const void *ws, size_t ws_bytes,
-                               Path *path) {
+// Descriptor, tensor pointers and the path an F-layer call takes.
+idxc_status check_indexer_tensors(const idxc_indexer_desc *d, const void *q, const void *k, const void *w,
+                                  const int32_t *t, const float *scores_dbg, Path *path) {
     idxc_status st = check_indexer_desc(d);
     if (st != IDXC_OK) return st;
     if (!q || !k || !w || !t) return IDXC_ERR_NULL;
@@ -92,6 +93,15 @@ idxc_status check_indexer_call(const idxc_indexer_desc *d, const void *q, const 
     const idxc::IndexerArgs a = make_args(d, q, k, w, nullptr, nullptr);
     *path = choose_path(a);
     if (*path == Path::None) return IDXC_ERR_UNSUPPORTED;
+    return IDXC_OK;
+}
+
+// Validation of the tensors of an F-layer call; shared by score_topk and route.
+idxc_status check_indexer_call(const idxc_indexer_desc *d, const void *q, const void *k, const void *w,
+                               const int32_t *t, const float *scores_dbg, const void *ws, size_t ws_bytes,
+                               Path *path) {
+    const idxc_status st = check_indexer_tensors(d, q, k, w, t, scores_dbg, path);
+    if (st != IDXC_OK) return st;
     if (*path == Path::Decode) {
         if (!ws || ws_bytes < decode_ws_bytes(d)) return IDXC_ERR_WORKSPACE;
         if (!aligned(ws, 16)) return IDXC_ERR_ALIGN;
@@ -329,6 +339,33 @@ PagedMlaWs paged_mla_ws(const idxc_paged_mla_desc *d, size_t mla_bytes) {
     return w;
 }
 
+// ---------------------------------------------------------------- static scratch
+//
+// Device memory of idx_score_topk_noalloc: one array per GPU, loaded with the
+// library's code object and held until the process ends.  Host code never
+// uses the array's name as an address (on the host it is only a stand-in):
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (resolved on its first use).
+idxc_status scratch_for_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return IDXC_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return IDXC_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return IDXC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,6 +383,7 @@ const char *idxc_status_str(idxc_status s) {
     case IDXC_ERR_WORKSPACE: return "workspace missing or too small";
     case IDXC_ERR_PATTERN: return "invalid layer pattern or layer index";
     case IDXC_ERR_HIP: return "HIP runtime error at launch";
+    case IDXC_ERR_SCRATCH: return "request needs more device scratch than the library's static array holds";
     }
     return "unknown status";
 }
@@ -367,6 +405,25 @@ idxc_status idx_score_topk(const idxc_indexer_desc *desc, const void *q, const v
     idxc_status st = check_indexer_call(desc, q, k, w, t_out, scores_dbg, ws, ws_bytes, &path);
     if (st != IDXC_OK) return st;
     return run_indexer(desc, q, k, w, t_out, scores_dbg, ws, path, static_cast<hipStream_t>(stream));
+}
+
+idxc_status idx_score_topk_noalloc(const idxc_indexer_desc *desc, const void *q, const void *k, const void *w,
+                                   int32_t *t_out, void *stream) {
+    // the same checks and kernels as idx_score_topk, with the static scratch as
+    // the workspace; nothing in it needs to start at zero (every word a call
+    // reads was written earlier in the same call).  All checks run before the
+    // first HIP call.
+    Path path;
+    idxc_status st = check_indexer_tensors(desc, q, k, w, t_out, nullptr, &path);
+    if (st != IDXC_OK) return st;
+    const size_t need = path == Path::Decode ? decode_ws_bytes(desc) : 0;
+    if (need > kScratchBytes) return IDXC_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        st = scratch_for_current_device(&ws);
+        if (st != IDXC_OK) return st;
+    }
+    return run_indexer(desc, q, k, w, t_out, nullptr, ws, path, static_cast<hipStream_t>(stream));
 }
 
 idxc_status idx_topk_workspace(int R, int Lk, int topk, size_t *bytes) {

@@ -15,7 +15,7 @@ import sparse_attention_indexer_lightning_amd as sa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "idxcache.h")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, PATTERN = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, PATTERN, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -9
 BF16, FP8, FP32 = 1, 2, 3
 FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
 FAKE_ODD = ctypes.c_void_p(0x10008)   # 8-byte aligned only
@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings():
     L = sa.lib()
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert L.idxc_status_str(code)
     assert L.idxc_status_str(5) == b"unknown status"
 
@@ -423,3 +423,27 @@ def test_binding_rejects_mismatched_paged_mla_tensors(bad):
         kw["lse"] = m(3, 64, dtype=F32)
     with pytest.raises(ValueError):
         sa.sparse_mla_attn_paged(q, kvc, table, qs, sl, t, 0.04, 512, **kw)
+
+
+def noalloc(d, q=FAKE, k=FAKE, w=FAKE, t=FAKE):
+    return sa.lib().idx_score_topk_noalloc(ctypes.byref(d) if d is not None else None, q, k, w, t, None)
+
+
+def test_noalloc_validates_before_any_hip_call():
+    d = desc(B=4, Lq=1, Lk=200000, topk=2048)
+    assert noalloc(None) == NULL
+    assert noalloc(d, q=None) == NULL
+    assert noalloc(d, t=FAKE_ODD) == ALIGN
+    assert noalloc(desc(H=12)) == UNSUP
+    # 64 sequences x 4 queries x 200,000 keys of fp32 scores: more than the
+    # 128 MiB static scratch
+    assert noalloc(desc(B=64, Lq=4, Lk=200000, topk=2048)) == SCRATCH
+    assert sa.lib().idxc_status_str(SCRATCH).startswith(b"request needs more device scratch")
+
+
+def test_binding_noalloc_requires_t_out():
+    q, k, w = idx_args()
+    with pytest.raises(ValueError):
+        sa.idx_score_topk_noalloc(q, k, w, 64, None)
+    with pytest.raises(ValueError):
+        sa.idx_score_topk_noalloc(q, k, w, 64, m(1, 128, 32, dtype=I32))
