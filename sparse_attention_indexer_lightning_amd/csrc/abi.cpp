@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/idxcache.h"
@@ -216,13 +217,40 @@ int log2i(int v) {
 }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Paged indexer workspace: row (sequence, position) pairs, row positions,
-// score rows of max_seq_len, then the row top-k's workspace.
+// The dense descriptor that the split-key scoring path sees for a serving
+// batch: total_q rows of one "sequence" whose score rows are max_seq_len long.
+idxc_indexer_desc paged_as_dense(const idxc_paged_indexer_desc *d);
+
+// Two ways to score a serving batch, chosen from the descriptor alone:
+//  * fused: the prefill kernel with page lookups per 64-key block scores and
+//    selects every row without storing scores (one workgroup per 8 rows of
+//    a sequence, so it pays off when the batch holds prefill chunks: more
+//    than 4 rows per sequence on average, fp8 with 64 heads of 128);
+//  * split: every row's keys split over many workgroups into score rows of
+//    max_seq_len, then the row top-k (decode tokens).
+bool paged_fused(const idxc_paged_indexer_desc *d) {
+    if ((long long)d->total_q <= 4LL * d->num_seqs) return false;
+    const idxc_indexer_desc e = paged_as_dense(d);
+    idxc::IndexerArgs a;
+    a.B = 1; a.Lq = 1; a.Lk = d->max_seq_len; a.H = d->H; a.D = d->D; a.topk = d->topk;
+    a.qk_enc = e.q_dtype == IDXC_FP8_E4M3 ? Enc::FP8 : Enc::BF16;
+    a.w_enc = e.w_dtype == IDXC_BF16 ? Enc::BF16 : Enc::FP32;
+    return e.q_dtype == IDXC_FP8_E4M3 && idxc::paged_prefill_supported(a);
+}
+
+// Paged indexer workspace.  Split: row (sequence, position) pairs, row
+// positions, score rows of max_seq_len, then the row top-k's workspace.
+// Fused: the row-block prefix over sequences only.
 struct PagedIdxWs {
-    size_t info, pos, scores, topk, total;
+    size_t info, pos, scores, topk, rb, total;
 };
 PagedIdxWs paged_idx_ws(const idxc_paged_indexer_desc *d) {
-    PagedIdxWs w;
+    PagedIdxWs w = {};
+    if (paged_fused(d)) {
+        w.rb = 0;
+        w.total = align256((size_t)(d->num_seqs + 1) * 4);
+        return w;
+    }
     w.info = 0;
     w.pos = align256((size_t)d->total_q * 8);
     w.scores = w.pos + align256((size_t)d->total_q * 4);
@@ -231,8 +259,6 @@ PagedIdxWs paged_idx_ws(const idxc_paged_indexer_desc *d) {
     return w;
 }
 
-// The dense descriptor that the split-key scoring path sees for a serving
-// batch: total_q rows of one "sequence" whose score rows are max_seq_len long.
 idxc_indexer_desc paged_as_dense(const idxc_paged_indexer_desc *d) {
     idxc_indexer_desc e;
     e.B = 1;
@@ -269,6 +295,26 @@ idxc_status run_indexer_paged(const idxc_paged_indexer_desc *d, const void *q, c
                               const void *w, int32_t *t, void *ws, hipStream_t stream) {
     const PagedIdxWs lay = paged_idx_ws(d);
     unsigned char *wsb = static_cast<unsigned char *>(ws);
+    if (paged_fused(d)) {
+        const idxc_indexer_desc dd = paged_as_dense(d);
+        idxc::IndexerArgs a = make_args(&dd, q, k_cache, w, t, nullptr);
+        idxc::PagedPrefill pp;
+        pp.query_start = query_start;
+        pp.seq_lens = seq_lens;
+        pp.block_table = block_table;
+        pp.rb_start = reinterpret_cast<int32_t *>(wsb + lay.rb);
+        pp.num_seqs = d->num_seqs;
+        pp.total_q = d->total_q;
+        pp.bs_log2 = log2i(d->block_size);
+        pp.max_blocks = d->max_blocks;
+        pp.num_blocks = d->num_blocks;
+        const long long cap = std::min<long long>(d->max_seq_len, (long long)d->max_blocks << pp.bs_log2);
+        hipError_t e = idxc::launch_row_blocks(query_start, d->num_seqs, d->total_q,
+                                               idxc::prefill_rows_per_workgroup(a), (int)cap,
+                                               reinterpret_cast<int32_t *>(wsb + lay.rb), stream);
+        if (e != hipSuccess) return IDXC_ERR_HIP;
+        return from_hip(idxc::launch_indexer_prefill_paged(a, pp, stream));
+    }
     int32_t *info = reinterpret_cast<int32_t *>(wsb + lay.info);
     int32_t *pos = reinterpret_cast<int32_t *>(wsb + lay.pos);
     float *scores = reinterpret_cast<float *>(wsb + lay.scores);

@@ -675,6 +675,14 @@ struct PrefillParams {
     int B, Lq, Lk, topk, cap;
     int nthreads;   // == blockDim.x, passed as an argument so it lives in an SGPR
     Enc w_enc;
+    // serving batch over a paged key cache (the Paged kernels): sequence b owns
+    // packed query rows query_start[b] .. query_start[b+1]-1, its last q_len
+    // positions of seq_lens[b]; its keys live in pages block_table[b][s >> bs_log2]
+    // of the pool k [num_blocks][1 << bs_log2][D]; its row blocks are
+    // workgroups rb_start[b] .. rb_start[b+1]-1.  Lq and Lk above are then the
+    // largest q_len and seq_len allowed.
+    const int32_t *query_start, *seq_lens, *block_table, *rb_start;
+    int num_seqs, bs_log2, max_blocks, num_blocks;
 };
 
 // LDS plan of the prefill kernel; identical on host and device.
@@ -707,7 +715,7 @@ __host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, 
     return L;
 }
 
-template <Enc E, int D, int H, typename IdxT>
+template <Enc E, int D, int H, typename IdxT, bool Paged>
 __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillParams p) {
     using S = Shape<E, D>;
     constexpr int TW = 64 / H;              // query rows per wave
@@ -732,20 +740,59 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     uint32_t *bkey_all = reinterpret_cast<uint32_t *>(smem + L.bkey);
     IdxT *bidx_all = reinterpret_cast<IdxT *>(smem + L.bidx);
 
-    // heaviest row blocks (largest positions) are dispatched first
-    const int nrb = (p.Lq + R - 1) / R;
-    const int rb = nrb - 1 - (int)(blockIdx.x / p.B);
-    const int b = (int)(blockIdx.x % p.B);
+    // This workgroup's sequence b, its query count Lq and key count Lk, the
+    // packed index row0 of its query 0 in q, w and t_out, and its row block
+    // rb.  Heaviest row blocks (largest positions) are dispatched first.
+    int b, Lq, Lk, rb;
+    size_t row0;
+    if constexpr (Paged) {
+        const int wg = (int)blockIdx.x;
+        if (wg >= p.rb_start[p.num_seqs]) return;   // the grid is an upper bound on the row blocks
+        int lo = 0, hi = p.num_seqs - 1;            // last sequence with rb_start <= wg
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.rb_start[mid] <= wg) lo = mid;
+            else hi = mid - 1;
+        }
+        b = lo;
+        // out-of-contract metadata is clamped (as the row-block count was) so
+        // that every row lies in the packed rows (p.Lq = total_q), every key
+        // in the pages the table can name and within the longest sequence
+        const int q0 = min(max(p.query_start[b], 0), p.Lq);
+        const int q1 = min(max(p.query_start[b + 1], q0), p.Lq);
+        const int lk_cap = min(p.Lk, p.max_blocks << p.bs_log2);
+        Lq = min(q1 - q0, lk_cap);
+        Lk = min(max(p.seq_lens[b], Lq), lk_cap);
+        row0 = (size_t)q0;
+        rb = (Lq + R - 1) / R - 1 - (wg - p.rb_start[b]);
+    } else {
+        Lq = p.Lq;
+        Lk = p.Lk;
+        const int nrb = (Lq + R - 1) / R;
+        rb = nrb - 1 - (int)(blockIdx.x / p.B);
+        b = (int)(blockIdx.x % p.B);
+        row0 = (size_t)b * Lq;
+    }
     const int i0 = rb * R;
-    const int off = p.Lk - p.Lq;
-    const int pmax = off + min(i0 + R, p.Lq) - 1;
+    const int off = Lk - Lq;
+    const int pmax = off + min(i0 + R, Lq) - 1;
     const int nblk = pmax / KB + 1;
+    // paged: the page of the 64-key block holding key s (pages hold a power of
+    // two >= 64 keys, so a block lies in one page); pages are clamped to the
+    // pool.  The table is read through the constant address space, so its
+    // loads are uniform scalar loads, off the vector-memory counter.
+    const __attribute__((address_space(4))) int32_t *btab =
+        Paged ? (const __attribute__((address_space(4))) int32_t *)(p.block_table + (size_t)b * p.max_blocks) : nullptr;
+    auto page_of = [&](int s) -> const unsigned char * {
+        const int pg = min(max(btab[s >> p.bs_log2], 0), p.num_blocks - 1);
+        return p.k + ((size_t)pg << p.bs_log2) * S::ROWB;
+    };
 
     Q32 Q32f;
     if constexpr (kMfma32) {
         const int i = i0 + wave;
-        if (i < p.Lq) {
-            const size_t qi = (size_t)b * p.Lq + i;
+        if (i < Lq) {
+            const size_t qi = row0 + i;
             load_q32(Q32f, p.q + qi * H * S::ROWB, [&](int h) { return load_w(p.w, p.w_enc, qi * H + h); }, lane);
         } else {
             load_q32(Q32f, p.q, [&](int h) { return 0.f; }, lane);
@@ -764,8 +811,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     for (int f = 0; f < 4 && !kMfma32; ++f) {
         const int r = 16 * f + n, t = r / H, h = r % H;
         const int i = i0 + wave * TW + t;
-        if (i < p.Lq) {
-            const size_t qrow = ((size_t)(b * (size_t)p.Lq + i) * H + h) * S::ROWB;
+        if (i < Lq) {
+            const size_t qrow = ((row0 + i) * H + h) * S::ROWB;
             load_frag<E, D>(A[f], p.q + qrow, g);
         } else {
             zero_frag<E, D>(A[f]);
@@ -774,7 +821,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         for (int ii = 0; ii < 4; ++ii) {
             const int ro = 16 * f + 4 * g + ii, to = ro / H, ho = ro % H;
             const int io = i0 + wave * TW + to;
-            wv[f][ii] = io < p.Lq ? load_w(p.w, p.w_enc, ((size_t)b * p.Lq + io) * H + ho) : 0.f;
+            wv[f][ii] = io < Lq ? load_w(p.w, p.w_enc, (row0 + io) * H + ho) : 0.f;
         }
     }
     for (int t = lane; t < TW; t += kWave) {
@@ -792,15 +839,22 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     constexpr int CPK = S::ROWB / 16;               // chunks per key
     const int nchunk = KB * CPK;
     const int cpt = (nchunk + p.nthreads - 1) / p.nthreads;
-    const unsigned char *kseq = p.k + (size_t)b * p.Lk * S::ROWB;
+    const unsigned char *kseq = Paged ? p.k : p.k + (size_t)b * Lk * S::ROWB;
     v4i kreg[kChunkMax];
     auto fetch = [&](int blk) {
+        // paged: the page of the block (of the last key for a block past it)
+        const unsigned char *pb = nullptr;
+        if constexpr (Paged) pb = page_of(min(blk * KB, Lk - 1));
 #pragma unroll
         for (int c = 0; c < kChunkMax; ++c) {
             if (c < cpt) {
                 const int ci = min(tid + c * p.nthreads, nchunk - 1);
-                const int key = min(blk * KB + ci / CPK, p.Lk - 1);
-                kreg[c] = *reinterpret_cast<const v4i *>(kseq + (size_t)key * S::ROWB + (ci % CPK) * 16);
+                const int key = min(blk * KB + ci / CPK, Lk - 1);
+                if constexpr (Paged)
+                    kreg[c] = *reinterpret_cast<const v4i *>(
+                        pb + (size_t)(key & ((1 << p.bs_log2) - 1)) * S::ROWB + (ci % CPK) * 16);
+                else
+                    kreg[c] = *reinterpret_cast<const v4i *>(kseq + (size_t)key * S::ROWB + (ci % CPK) * 16);
             }
         }
     };
@@ -821,9 +875,9 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     auto select_binned = [&](float sc, int base) -> bool {
         const int i = i0 + wave;
         const int pos = off + i;
-        if (i >= p.Lq || base > pos) return false;
+        if (i >= Lq || base > pos) return false;
         const int s = base + lane;
-        if (p.scores && s < p.Lk) p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc : -INFINITY;
+        if (p.scores && s < Lk) p.scores[(row0 + i) * Lk + s] = s <= pos ? sc : -INFINITY;
         const bool cand = s <= pos && sc > st.thr_f;
         const uint64_t m = ballot(cand);
         if (m) {
@@ -859,7 +913,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     };
 
     // last position among this wave's valid rows (for skipping blocks)
-    const int wlast = min(i0 + wave * TW + TW, p.Lq) - 1;
+    const int wlast = min(i0 + wave * TW + TW, Lq) - 1;
     const int wpmax = off + wlast;
     const bool wave_has_rows = wlast >= i0 + wave * TW;
 
@@ -887,21 +941,26 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         // the owning rows' selection an iteration later.
         const int jq = wave & 1, sq = wave >> 1;
         float inv_s_lin;
-        const v8i Alin = linear_terms_frag(p.q, p.w, p.w_enc, (size_t)b * p.Lq + i0, p.Lq - i0, jq, lane, inv_s_lin);
+        const v8i Alin = linear_terms_frag(p.q, p.w, p.w_enc, row0 + i0, Lq - i0, jq, lane, inv_s_lin);
         float *linbuf = reinterpret_cast<float *>(smem + L.stage);   // [2][8 rows][64 keys]
         const int lin_put = (4 * jq + (lane >> 4)) * KB + 16 * sq + (lane & 15);
         const int lin_get = wave * KB + lane;
         constexpr int CPK = S::ROWB / 16;
         static_assert(KB * CPK == kMaxThreads, "one 16-byte chunk per thread and key block");
-        const unsigned char *kseq = p.k + (size_t)b * p.Lk * S::ROWB;
         const int krow = tid / CPK, kcol = (tid % CPK) * 16;
         auto fetch1 = [&](int blk) {
-            const int key = min(blk * KB + krow, p.Lk - 1);   // past Lk: clamped, never used
-            // 32-bit offset from the sequence's base (this sweep runs with 16-bit
-            // key indices, so at most 65536 keys of 128 bytes):
-            // one VALU add instead of 64-bit address arithmetic per staging load
-            const uint32_t off = (uint32_t)key * (uint32_t)S::ROWB + (uint32_t)kcol;
-            return *reinterpret_cast<const v4i *>(kseq + off);
+            const int key = min(blk * KB + krow, Lk - 1);   // past Lk: clamped, never used
+            // 32-bit offset from the sequence's base, or from the block's page
+            // (this sweep runs with 16-bit key indices, so at most 65536 keys
+            // of 128 bytes): one VALU add instead of 64-bit address arithmetic
+            if constexpr (Paged) {
+                const unsigned char *pb = page_of(min(blk * KB, Lk - 1));
+                const uint32_t o = (uint32_t)(key & ((1 << p.bs_log2) - 1)) * (uint32_t)S::ROWB + (uint32_t)kcol;
+                return *reinterpret_cast<const v4i *>(pb + o);
+            } else {
+                const uint32_t o = (uint32_t)key * (uint32_t)S::ROWB + (uint32_t)kcol;
+                return *reinterpret_cast<const v4i *>(kseq + o);
+            }
         };
         auto stash1 = [&](int buf, const v4i &v) {
             *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + krow * S::PITCH + kcol) = v;
@@ -929,7 +988,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         auto bmap = [&](int it) { return it < ns ? it * kSampleStride : it - ns; };
         auto tau_step = [&]() {
             const int i = i0 + wave;
-            if (i >= p.Lq) return;
+            if (i >= Lq) return;
             const int pos = off + i;
             int nsk = 0;   // sampled keys at or before the row's position
             for (int j = 0; j < ns; ++j) {
@@ -1031,7 +1090,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         if (ns == 0) break;
         {
             const int i = i0 + wave;
-            if (i < p.Lq && off + i + 1 > p.topk && st.cnt < p.topk && lane == 0) atomicOr(&flags[3], 1);
+            if (i < Lq && off + i + 1 > p.topk && st.cnt < p.topk && lane == 0) atomicOr(&flags[3], 1);
         }
         __syncthreads();
         const bool again = flags[3] != 0;
@@ -1144,13 +1203,13 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
                 for (int t = 0; t < TW; ++t) {
                     const int i = i0 + wave * TW + t;
-                    if (i >= p.Lq) continue;
+                    if (i >= Lq) continue;
                     const int pos = off + i;
                     if (base > pos) continue;
                     const int s = base + lane;
                     const int row = wave * TW + t;
-                    if (p.scores && s < p.Lk)
-                        p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = s <= pos ? sc[t] : -INFINITY;
+                    if (p.scores && s < Lk)
+                        p.scores[(row0 + i) * Lk + s] = s <= pos ? sc[t] : -INFINITY;
                     int cnt = rcnt[row];
                     uint32_t thr = rthr[row];
                     const uint32_t key = score_key(sc[t]);
@@ -1182,18 +1241,18 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // final selection and output
     for (int t = 0; t < TW; ++t) {
         const int i = i0 + wave * TW + t;
-        if (i >= p.Lq) break;
+        if (i >= Lq) break;
         const int row = wave * TW + t;
         uint32_t *bk = bkey_all + (size_t)row * p.cap;
         IdxT *bi = bidx_all + (size_t)row * p.cap;
         int cnt = kBinned ? st.cnt : rcnt[row];
         if (cnt > p.topk) (void)select_compact<IdxT>(bk, bi, cnt, p.topk, hist, lane);
-        int32_t *o = p.t_out + ((size_t)b * p.Lq + i) * p.topk;
+        int32_t *o = p.t_out + (row0 + i) * p.topk;
         for (int j = lane; j < p.topk; j += kWave) o[j] = j < cnt ? (int32_t)bi[j] : -1;
         if (p.scores) {
             const int pos = off + i;
-            for (int s = (pos / KB + 1) * KB + lane; s < p.Lk; s += kWave)
-                p.scores[((size_t)b * p.Lq + i) * p.Lk + s] = -INFINITY;
+            for (int s = (pos / KB + 1) * KB + lane; s < Lk; s += kWave)
+                p.scores[(row0 + i) * Lk + s] = -INFINITY;
         }
     }
 }
@@ -1408,13 +1467,14 @@ void decode_scores_kernel(ScoreParams p) {
     write_bound();
 }
 
-template <Enc E, int D, int H, typename IdxT>
-hipError_t launch_prefill_t(const IndexerArgs &a, int waves, int cap, size_t lds, hipStream_t st) {
-    auto kern = prefill_kernel<E, D, H, IdxT>;
+template <Enc E, int D, int H, typename IdxT, bool Paged = false>
+hipError_t launch_prefill_t(const IndexerArgs &a, int waves, int cap, size_t lds, hipStream_t st,
+                            const PagedPrefill *pp = nullptr) {
+    auto kern = prefill_kernel<E, D, H, IdxT, Paged>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    PrefillParams p;
+    PrefillParams p = {};
     p.q = static_cast<const unsigned char *>(a.q);
     p.k = static_cast<const unsigned char *>(a.k);
     p.w = a.w;
@@ -1424,8 +1484,22 @@ hipError_t launch_prefill_t(const IndexerArgs &a, int waves, int cap, size_t lds
     p.nthreads = waves * kWave;
     p.w_enc = a.w_enc;
     const int R = waves * (64 / H);
-    const int nrb = (a.Lq + R - 1) / R;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(nrb * a.B)), dim3(waves * kWave), lds, st, p);
+    unsigned grid;
+    if constexpr (Paged) {
+        p.query_start = pp->query_start;
+        p.seq_lens = pp->seq_lens;
+        p.block_table = pp->block_table;
+        p.rb_start = pp->rb_start;
+        p.num_seqs = pp->num_seqs;
+        p.bs_log2 = pp->bs_log2;
+        p.max_blocks = pp->max_blocks;
+        p.num_blocks = pp->num_blocks;
+        // at most ceil(q_len / R) <= q_len / R + 1 row blocks per sequence
+        grid = (unsigned)((pp->total_q + R - 1) / R + pp->num_seqs);
+    } else {
+        grid = (unsigned)(((a.Lq + R - 1) / R) * a.B);
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, st, p);
     return hipGetLastError();
 }
 
@@ -1561,6 +1635,25 @@ hipError_t launch_decode_d(const IndexerArgs &a, hipStream_t st, const PagedKeys
 }  // namespace
 
 bool prefill_fits(const IndexerArgs &a) { return plan_prefill(a).ok; }
+
+int prefill_rows_per_workgroup(const IndexerArgs &a) {
+    const PrefillPlan pl = plan_prefill(a);
+    return pl.ok ? pl.waves * (64 / a.H) : 0;
+}
+
+bool paged_prefill_supported(const IndexerArgs &a) {
+    return a.qk_enc == Enc::FP8 && a.D == 128 && a.H == 64 && prefill_fits(a);
+}
+
+hipError_t launch_indexer_prefill_paged(const IndexerArgs &a, const PagedPrefill &pp, hipStream_t st) {
+    if (!paged_prefill_supported(a)) return hipErrorInvalidValue;
+    const PrefillPlan pl = plan_prefill(a);
+    if (pl.idx_bytes == 2) {
+        if (pl.waves * kWave != kMaxThreads) return hipErrorInvalidConfiguration;
+        return launch_prefill_t<Enc::FP8, 128, 64, uint16_t, true>(a, pl.waves, pl.cap, pl.lds, st, &pp);
+    }
+    return launch_prefill_t<Enc::FP8, 128, 64, uint32_t, true>(a, pl.waves, pl.cap, pl.lds, st, &pp);
+}
 
 hipError_t launch_indexer_prefill(const IndexerArgs &a, hipStream_t st) {
     if (a.qk_enc == Enc::FP8) {

@@ -36,6 +36,25 @@ struct PagedKeys {
     int bs_log2, max_blocks, num_blocks;
 };
 
+// Fused score + top-k of a serving batch over a paged key cache (fp8, 64
+// heads, d 128): a.q / a.w / a.t_out are packed rows [total_q, ...], a.k the
+// page pool, a.Lk the longest sequence; rb_start [num_seqs + 1] (from
+// launch_row_blocks with the same rows per workgroup) maps workgroups to
+// (sequence, row block).  Rows of a sequence are its last q_len positions.
+struct PagedPrefill {
+    const int32_t *query_start, *seq_lens, *block_table;
+    const int32_t *rb_start;
+    int num_seqs, total_q, bs_log2, max_blocks, num_blocks;
+};
+bool paged_prefill_supported(const IndexerArgs &a);
+int prefill_rows_per_workgroup(const IndexerArgs &a);
+hipError_t launch_indexer_prefill_paged(const IndexerArgs &a, const PagedPrefill &pp, hipStream_t s);
+// rb_start[b] = sum over sequences b' < b of ceil(q_len_b' / rows), with the
+// query starts clamped to [0, total_q] and q_len to lk_cap as the paged
+// prefill kernel clamps them; one workgroup.
+hipError_t launch_row_blocks(const int32_t *query_start, int B, int total_q, int rows, int lk_cap,
+                             int32_t *rb_start, hipStream_t s);
+
 // Scores of every (query, key <= position) into a.scores [B*Lq, Lk], keys
 // split over many workgroups; -inf beyond each query's position.
 bool decode_supported(const IndexerArgs &a);

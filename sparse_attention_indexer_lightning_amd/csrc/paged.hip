@@ -59,7 +59,50 @@ __global__ void translate_kernel(const int32_t *t, const int32_t *row_info, cons
     out[e] = v;
 }
 
+// Prefix of row blocks over sequences (one workgroup of 1024 threads, the
+// sequences in chunks of 1024: a wavefront scan, then the wavefront totals).
+__global__ __launch_bounds__(1024) void row_blocks_kernel(const int32_t *qs, int B, int total_q, int rows,
+                                                          int lk_cap, int32_t *rb_start) {
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    int carry = 0;
+    for (int c0 = 0; c0 < B; c0 += 1024) {
+        const int b = c0 + tid;
+        int n = 0;
+        if (b < B) {
+            // the clamps of the paged prefill kernel
+            const int q0 = min(max(qs[b], 0), total_q);
+            const int q1 = min(max(qs[b + 1], q0), total_q);
+            n = (min(q1 - q0, lk_cap) + rows - 1) / rows;
+        }
+        int incl = n;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int t = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += t;
+        }
+        if (lane == kWave - 1) wsum[wave] = incl;
+        __syncthreads();
+        int before = 0, total = 0;
+        for (int w = 0; w < 16; ++w) {
+            if (w < wave) before += wsum[w];
+            total += wsum[w];
+        }
+        if (b < B) rb_start[b] = carry + before + incl - n;
+        carry += total;
+        __syncthreads();   // wsum is rewritten by the next chunk
+    }
+    if (tid == 0) rb_start[B] = carry;
+}
+
 }  // namespace
+
+hipError_t launch_row_blocks(const int32_t *query_start, int B, int total_q, int rows, int lk_cap,
+                             int32_t *rb_start, hipStream_t s) {
+    hipLaunchKernelGGL(row_blocks_kernel, dim3(1), dim3(1024), 0, s, query_start, B, total_q, rows, lk_cap,
+                       rb_start);
+    return hipGetLastError();
+}
 
 hipError_t launch_row_info(const int32_t *query_start, const int32_t *seq_lens, int B, int rows, int max_pos,
                            int32_t *row_info, int32_t *row_pos, hipStream_t s) {

@@ -447,3 +447,23 @@ def test_binding_noalloc_requires_t_out():
         sa.idx_score_topk_noalloc(q, k, w, 64, None)
     with pytest.raises(ValueError):
         sa.idx_score_topk_noalloc(q, k, w, 64, m(1, 128, 32, dtype=I32))
+
+
+def paged_ws(**kw):
+    d = pdesc(**kw)
+    n = ctypes.c_size_t(0)
+    assert sa.lib().idx_score_topk_paged_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
+    return n.value
+
+
+def test_paged_workspace_by_mode():
+    """Prefill-heavy batches (more than 4 rows per sequence, fp8 64 x 128) take the
+    fused kernel and need only the row-block prefix; decode batches keep the
+    split path's score rows."""
+    fused = paged_ws(num_seqs=4, total_q=4800, max_seq_len=200000, num_blocks=4000, block_size=64, max_blocks=3200)
+    assert fused <= 256
+    split = paged_ws(num_seqs=4, total_q=16, max_seq_len=200000, num_blocks=4000, block_size=64, max_blocks=3200)
+    assert split >= 16 * 200000 * 4
+    bf16 = paged_ws(num_seqs=4, total_q=4800, max_seq_len=20000, num_blocks=4000, block_size=64, max_blocks=400,
+                    qd=BF16, kd=BF16, wd=FP32, D=64)
+    assert bf16 >= 4800 * 20000 * 4    # the fused paged form is fp8-only: split path

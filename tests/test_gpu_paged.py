@@ -102,6 +102,60 @@ def test_paged_route_full_then_shared():
     assert torch.equal(ref, first)
 
 
+# ---- prefill chunks: the fused kernel with page lookups (more than four rows
+# per sequence on average, fp8 with 64 heads of 128)
+
+def test_paged_fused_prefill_equals_contiguous():
+    """One sequence whose rows are all its positions, pages at random slots:
+    the fused paged path runs the same arithmetic as the contiguous fused
+    kernel on the gathered keys, so T is identical."""
+    L, topk = 6000, 2048
+    q, k_cache, w, table, qs, sl = make_batch([L], [L], 64, 128, torch.float8_e4m3fn, seed=21)
+    kc = contiguous_keys(k_cache, table[0], L)[None]
+    t_dense = sa.idx_score_topk(q.view(1, L, 64, 128), kc, w.view(1, L, 64), topk)
+    t_paged = sa.idx_score_topk_paged(q, k_cache, table, qs, sl, w, topk, max_seq_len=L)
+    torch.cuda.synchronize()
+    assert torch.equal(t_dense.view(L, topk), t_paged)
+
+
+def _check_batch_sampled(q, k_cache, w, table, qs, sl, t, seq_lens, topk, n_rows, seed):
+    tg = t.cpu().numpy()
+    qr, kr, wr = raw(q), raw(k_cache), raw(w)
+    dts = (enc_of(q), enc_of(k_cache), enc_of(w))
+    tb, qsn = table.cpu().numpy(), qs.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    for b, L in enumerate(seq_lens):
+        r0, r1 = int(qsn[b]), int(qsn[b + 1])
+        n = r1 - r0
+        if n == 0:
+            continue
+        local = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(n, n_rows), replace=False)]))
+        kb = oracle.gather_pages(kr, tb[b], L)[None]
+        to, so = oracle.indexer_topk(qr[None, r0:r1], kb, wr[None, r0:r1], dts, topk, rows=local)
+        pos = oracle.row_positions(1, n, L, local)
+        check_index_sets(tg[r0 + local], to, so, pos, topk, RTOL["fp8"], what=f"seq {b}")
+
+
+def test_paged_fused_chunk_4k_vs_oracle():
+    """A serving batch with a 4096-query prefill chunk (the last 4096 positions
+    of a 20,000-token sequence), a shorter chunk and decode tokens, on
+    sampled rows of every sequence."""
+    seq_lens, q_lens, topk = [20000, 9000, 5000, 3333], [4096, 700, 1, 3], 2048
+    q, k_cache, w, table, qs, sl = make_batch(seq_lens, q_lens, 64, 128, torch.float8_e4m3fn, seed=22)
+    t = sa.idx_score_topk_paged(q, k_cache, table, qs, sl, w, topk, max_seq_len=20000)
+    torch.cuda.synchronize()
+    _check_batch_sampled(q, k_cache, w, table, qs, sl, t, seq_lens, topk, 40, seed=23)
+
+
+def test_paged_fused_beyond_16bit_keys_vs_oracle():
+    """A sequence past 65,536 keys takes the fused kernel's 32-bit index form."""
+    seq_lens, q_lens, topk = [70000, 1000], [600, 50], 2048
+    q, k_cache, w, table, qs, sl = make_batch(seq_lens, q_lens, 128, 128, torch.float8_e4m3fn, seed=24)
+    t = sa.idx_score_topk_paged(q, k_cache, table, qs, sl, w, topk, max_seq_len=70000)
+    torch.cuda.synchronize()
+    _check_batch_sampled(q, k_cache, w, table, qs, sl, t, seq_lens, topk, 12, seed=25)
+
+
 @pytest.mark.parametrize("Hq,bs", [(64, 16), (128, 64), (16, 64)])
 def test_paged_mla_vs_oracle(Hq, bs):
     seq_lens, q_lens, topk = [1000, 333, 2048], [1, 3, 2], 300
