@@ -199,6 +199,44 @@ def decode(args, torch, sa, inputs):
     }
 
 
+def serving_prefill_chunk(args, torch, sa, inputs):
+    """A serving batch holding one prefill chunk: the last 4096 positions of a
+    200,000-token sequence, its indexer keys in 64-row pages at random slots of
+    a pool.  Timed through idx_score_topk_paged (the fused kernel with page
+    lookups) next to idx_score_topk on the same rows over contiguous keys."""
+    import dataclasses
+    base = inputs.WORKLOADS["decode_200k"]
+    C, L = 4096, base.Lk
+    wl = dataclasses.replace(base, name="chunk", B=1, Lq=C)
+    dev = torch.device("cuda:0")
+    q, k, w = inputs.indexer_inputs(wl, 0, dev)
+    bs = 64
+    npg = (L + bs - 1) // bs
+    g = torch.Generator(device="cpu").manual_seed(12)
+    perm = torch.randperm(npg, generator=g).to(dev)
+    table = perm.view(1, npg).to(torch.int32)
+    k_pool = torch.empty(npg, bs, wl.D, dtype=k.dtype, device=dev)
+    k_pool[perm.long()] = k.view(npg, bs, wl.D)
+    qs = torch.tensor([0, C], dtype=torch.int32, device=dev)
+    sl = torch.tensor([L], dtype=torch.int32, device=dev)
+    qp, wp = q.view(C, wl.H, wl.D), w.view(C, wl.H)
+    ws_bytes = sa.idx_score_topk_paged_workspace(qp, k_pool, wp, table, qs, wl.topk, L)
+    wsp = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    tp = torch.empty(C, wl.topk, dtype=torch.int32, device=dev)
+    tc = torch.empty(1, C, wl.topk, dtype=torch.int32, device=dev)
+    ms_paged = time_steps(lambda: sa.idx_score_topk_paged(qp, k_pool, table, qs, sl, wp, wl.topk, L, t_out=tp,
+                                                          ws=wsp), 5, 1, torch)
+    ms_contig = time_steps(lambda: sa.idx_score_topk(q, k, w, wl.topk, t_out=tc), 5, 1, torch)
+    same = bool(torch.equal(tp, tc[0]))
+    pairs = causal_pairs(C, L)
+    del k_pool
+    return {"chunk_queries": C, "context": L, "block_size": bs, "pages": "random slots of one pool",
+            "paged_ms": round(ms_paged, 3), "contiguous_ms": round(ms_contig, 3),
+            "paged_pairs_per_s": round(pairs / (ms_paged * 1e-3), 1), "t_identical_to_contiguous": same,
+            "workspace_bytes": ws_bytes,
+            "note": "the fused kernel reads each 64-key block's page from the block table; no score rows stored"}
+
+
 def decode_layer_bytes(wl) -> int:
     """Algorithmic HBM bytes of one Full decode layer: every key of every
     sequence once, the selected latent rows once, the indexer queries and
@@ -446,6 +484,7 @@ def main():
     }
     if not args.no_decode:
         line["secondary"] = decode(args, torch, sa, inputs)
+        line["secondary"]["serving_prefill_chunk"] = serving_prefill_chunk(args, torch, sa, inputs)
     if not args.no_sweep:
         line["retention_sweep"] = retention_sweep(args, torch, sa, inputs)
     if not args.no_cpu_baseline:
