@@ -89,7 +89,7 @@ def headline(args, torch, sa, inputs):
     ms = time_steps(step, args.steps, args.warmup, torch)
     pairs = causal_pairs(wl.Lq, wl.Lk, wl.B)
     flops = pairs * wl.H * wl.D * 2
-    return wl, ms, pairs, flops
+    return wl, ms, pairs, flops, t_cache
 
 
 def decode(args, torch, sa, inputs):
@@ -397,10 +397,12 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(args, inputs, torch):
+def cpu_baseline(args, inputs, torch, t_gpu=None):
     """Oracle pairs/s on the host (bounded seeded row sample of prefill_64k):
     once on the CPU share this process is given (OMP_NUM_THREADS, else every
-    core), once on one thread."""
+    core), once on one thread.  With ``t_gpu`` (the timed steps' T) the
+    sampled rows' oracle T is also compared with it: mean and minimum share
+    of the oracle's k indices that the GPU selected, and rows identical."""
     import numpy as np
 
     import oracle
@@ -416,21 +418,38 @@ def cpu_baseline(args, inputs, torch):
     rng = np.random.default_rng(2024)
     order = rng.permutation(wl.Lq)
 
+    sampled = []   # (rows, oracle T)
+
     def run(nthreads, seconds, start):
         done_rows, done_pairs, wall = 0, 0, 0.0
         batch = 2 * nthreads
         while wall < seconds and start + done_rows < wl.Lq:
             rows = np.sort(order[start + done_rows:start + done_rows + batch]).astype(np.int64)
             t0 = time.perf_counter()
-            oracle.indexer_topk(qr, kr, wr, ("fp8", "fp8", "bf16"), wl.topk, rows=rows, nthreads=nthreads)
+            t_or, _ = oracle.indexer_topk(qr, kr, wr, ("fp8", "fp8", "bf16"), wl.topk, rows=rows, nthreads=nthreads)
             wall += time.perf_counter() - t0
+            sampled.append((rows, t_or))
             done_rows += rows.size
             done_pairs += int((rows + 1).sum())
         return done_rows, done_pairs, wall
 
     rows_n, pairs_n, wall_n = run(threads, args.cpu_seconds, 0)
     rows_1, pairs_1, wall_1 = run(1, args.cpu_seconds / 3, rows_n)
+    agreement = None
+    if t_gpu is not None:
+        rows = np.concatenate([r for r, _ in sampled])
+        t_or = np.concatenate([t for _, t in sampled])
+        t_g = t_gpu.reshape(-1, wl.topk)[torch.from_numpy(rows).to(t_gpu.device)].cpu().numpy()
+        share = []
+        for a, b in zip(t_g, t_or):
+            ref = b[b >= 0]
+            share.append(np.intersect1d(a[a >= 0], ref).size / max(ref.size, 1))
+        share = np.asarray(share)
+        agreement = {"rows": int(rows.size), "overlap_mean": round(float(share.mean()), 6),
+                     "overlap_min": round(float(share.min()), 6),
+                     "rows_identical": int(sum(np.array_equal(a, b) for a, b in zip(t_g, t_or)))}
     return {"value": round(pairs_n / wall_n, 1), "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "t_agreement_with_gpu": agreement,
             "sample": f"{rows_n} seeded random query rows of prefill_64k ({pairs_n} causal pairs, fp64 scores + "
                       f"top-k), {wall_n:.1f} s wall on {threads} threads",
             "host_cpu": _cpu_model(), "host_logical_cores": host_cores,
@@ -455,7 +474,7 @@ def main():
     if args.profile:
         profile_run(args, torch, sa, inputs)
         return
-    wl, ms, pairs, flops = headline(args, torch, sa, inputs)
+    wl, ms, pairs, flops, t_head = headline(args, torch, sa, inputs)
     if args.profile_only:
         print(json.dumps({"ms_per_step": ms}))
         return
@@ -488,7 +507,7 @@ def main():
     if not args.no_sweep:
         line["retention_sweep"] = retention_sweep(args, torch, sa, inputs)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args, inputs, torch)
+        line["cpu_baseline"] = cpu_baseline(args, inputs, torch, t_head)
     print(json.dumps(line))
 
 

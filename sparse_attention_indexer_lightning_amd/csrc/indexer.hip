@@ -962,8 +962,14 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                 return *reinterpret_cast<const v4i *>(kseq + o);
             }
         };
+        // Key tile swizzle: the 32-byte half h of key row r (16-byte chunks
+        // 2h, 2h+1) sits at half h ^ (r2 ^ r3 ^ r4).  A 16-byte LDS read
+        // serves together the 16 lanes with one value of (l5, l2 ^ l3 ^ l4);
+        // with the 144-byte pitch both operand reads below (32 rows x one
+        // half, 16 rows x four halves) then cover all 64 banks in each cycle.
+        auto kswz = [](int r) { return (__builtin_popcount(r & 28) & 1) << 5; };
         auto stash1 = [&](int buf, const v4i &v) {
-            *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + krow * S::PITCH + kcol) = v;
+            *reinterpret_cast<v4i *>(ktile + (size_t)buf * KB * S::PITCH + krow * S::PITCH + (kcol ^ kswz(krow))) = v;
         };
         auto combine = [](float p0, float p1) {
             // lanes 0-31 hold key fragment 0 of their head half, lanes 32-63 the other half
@@ -1029,8 +1035,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             for (int cf = 0; cf < 2; ++cf)
 #pragma unroll
                 for (int st2 = 0; st2 < 2; ++st2)
-                    B[cf][st2] = load32(kt + (32 * cf + (lane & 31)) * S::PITCH + 64 * st2 + 32 * (lane >> 5));
-            const v8i Bl = load32(kt + (16 * sq + (lane & 15)) * S::PITCH + 32 * (lane >> 4));
+                    B[cf][st2] = load32(kt + (32 * cf + (lane & 31)) * S::PITCH + ((64 * st2 + 32 * (lane >> 5)) ^ kswz(lane)));
+            const v8i Bl = load32(kt + (16 * sq + (lane & 15)) * S::PITCH + ((32 * (lane >> 4)) ^ kswz(16 * sq + (lane & 15))));
             const v4f dl = mfma_fp8_16x16x128(Alin, Bl, v4f{0.f, 0.f, 0.f, 0.f});
             v16f a0[2];
 #pragma unroll
