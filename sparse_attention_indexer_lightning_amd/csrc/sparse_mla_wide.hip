@@ -119,8 +119,11 @@ __device__ __forceinline__ float swap32_sum(float v) {
     return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+// two floats rounded to bf16 (nearest even) in one packed conversion, lo in bits 0-15
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
 }
 
 // Keeps a per-step copy of an LDS offset opaque, so that the compiler adds
@@ -278,17 +281,26 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
                 }
                 // rows of this lane: 16rb + 4g + i for register i of block rb;
                 // logits stay unscaled (z * sl2 is formed inside the exponent)
-                const bool vrow = RT * s + n < clen && ix_mask >= 0 && ix_mask < a.Lk;
+                const bool vrow = (RT * s + n < clen) & (ix_mask >= 0) & (ix_mask < a.Lk);
                 const uint32_t vball = (uint32_t)ballot(vrow && hh == 0);   // bit r: row r
                 const bool all_valid = vball == 0xFFFFFFFFu;
+                if (!all_valid) {
+                    // a partial tile (the set's tail, or entries outside the
+                    // cache); the empty asm keeps this a branch, so full tiles
+                    // run no per-element selects
+                    asm volatile("" ::: "memory");
+                    const uint32_t bits = vball >> (4 * g);   // bit 16rb + i: row 16rb + 4g + i
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (!((bits >> (16 * rb + i)) & 1u)) acc[rb][i] = -INFINITY;
+                }
                 float lm = -INFINITY;
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (!all_valid) acc[rb][i] = ((vball >> (16 * rb + 4 * g + i)) & 1u) ? acc[rb][i] : -INFINITY;
-                        lm = fmaxf(lm, acc[rb][i]);
-                    }
+                    for (int i = 0; i < 4; ++i) lm = fmaxf(lm, acc[rb][i]);
                 lm = swap32_max(swap16_max(lm)) * sl2;   // sl2 > 0: the maximum of the scaled logits
                 const float m_new = lm > m_ref + kSlack ? lm : m_ref;
                 const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
