@@ -101,14 +101,21 @@ __device__ __forceinline__ void fill_group(const unsigned char *src, lds_u8 *slo
     }
 }
 
+// v_max_f32 as is: fmaxf would first quieten both operands (two more
+// instructions per use), and no NaN reaches these maxima
+__device__ __forceinline__ float max_f32(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 __device__ __forceinline__ float swap32_max(float v) {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    return max_f32(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
 // maxima and sums over lanes l and l^16 (the 16-lane rows swapped pairwise)
 __device__ __forceinline__ float swap16_max(float v) {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    return max_f32(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
 __device__ __forceinline__ float swap16_sum(float v) {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -304,9 +311,11 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
                 lm = swap32_max(swap16_max(lm)) * sl2;   // sl2 > 0: the maximum of the scaled logits
                 const float m_new = lm > m_ref + kSlack ? lm : m_ref;
                 const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                if (g == 0) sm.alpha[par][H] = alpha;
+                // every lane stores: the four lanes of a head hold the same
+                // alpha, and the flag is uniform (no exec-mask changes)
+                sm.alpha[par][H] = alpha;
                 const bool raised = ballot(m_new != m_ref) != 0;
-                if (lane == 0) sm.flag[par][p] = raised ? 1 : 0;
+                sm.flag[par][p] = raised ? 1 : 0;
                 // exp2(-inf) = 0 takes care of masked rows whenever m_new is
                 // finite; m_new = -inf means no valid row so far (all zero)
                 const float mneg = m_new == -INFINITY ? 0.f : -m_new;
@@ -318,7 +327,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[rb][i], sl2, mneg));
-                        ps += pv[i];
+                        ps = rb == 0 && i == 0 ? pv[i] : ps + pv[i];   // (0 + p = p: p >= 0)
                     }
                     // rows 16rb + 4g..+3: half g%2 of chunk q = 2rb + g/2, chunk q
                     // of head H stored at 16((q + H/4) mod 4)
