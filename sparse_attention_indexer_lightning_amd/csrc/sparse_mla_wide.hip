@@ -256,33 +256,33 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_mla_wide_kernel(MlaWideA
                 for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                     for (int k = 0; k < 2; ++k) kbs[rb][k] = opaque(kb[rb][k]);
-                // software pipeline over pairs of k-steps: the reads of pair
-                // q+1 are in flight while pair q runs on the MFMA unit
+                // software pipeline over pairs of k-steps: the reads of pairs
+                // q+1 and q+2 are in flight while pair q runs on the MFMA unit
+                // (one pair of MFMAs does not cover the LDS latency when the
+                // four producers read at once)
                 v4f acc[2];
                 acc[0] = v4f{0.f, 0.f, 0.f, 0.f};
                 acc[1] = acc[0];
-                v4i kf[2][2][2];   // [buffer][k-step of the pair][row block]
+                v4i kf[3][2][2];   // [buffer][k-step of the pair][row block]
+                auto read_pair = [&](int q, v4i (&dst)[2][2]) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                    for (int i = 0; i < 2; ++i) {
+                        const int ks = 2 * q + i;
 #pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) kf[0][i][rb] = lds_read_b128(cur + kbs[rb][i & 1] + OCT_BYTES * (i >> 1));
+                        for (int rb = 0; rb < 2; ++rb) dst[i][rb] = lds_read_b128(cur + kbs[rb][ks & 1] + OCT_BYTES * (ks >> 1));
+                    }
+                };
+                read_pair(0, kf[0]);
+                read_pair(1, kf[1]);
 #pragma unroll
                 for (int q = 0; q < KS / 2; ++q) {
-                    if (q + 1 < KS / 2) {
-#pragma unroll
-                        for (int i = 0; i < 2; ++i) {
-                            const int ks = 2 * (q + 1) + i;
-#pragma unroll
-                            for (int rb = 0; rb < 2; ++rb)
-                                kf[(q + 1) & 1][i][rb] = lds_read_b128(cur + kbs[rb][ks & 1] + OCT_BYTES * (ks >> 1));
-                        }
-                    }
+                    if (q + 2 < KS / 2) read_pair(q + 2, kf[(q + 2) % 3]);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
                         for (int rb = 0; rb < 2; ++rb)
-                            acc[rb] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, kf[q & 1][i][rb]),
+                            acc[rb] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, kf[q % 3][i][rb]),
                                                          __builtin_bit_cast(v8bf, qf[2 * q + i]), acc[rb]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
