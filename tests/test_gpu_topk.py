@@ -51,6 +51,20 @@ def test_all_equal_rows():
         assert np.array_equal(t, np.tile(np.arange(2048, dtype=np.int32), (3, 1)))
 
 
+@pytest.mark.parametrize("R,Lk", [(1, 65536), (2, 70001)])
+def test_all_equal_rows_split_path(R, Lk):
+    """All-equal long rows take the split path with every key a candidate (more
+    than the LDS capacity: the HBM select runs); ties go to the lower index."""
+    for v in (0.0, 1.5):
+        s = np.full((R, Lk), v, np.float32)
+        if v == 0.0:
+            s[:, 1::2] = -0.0                     # -0 and +0 are equal keys
+        t = run(s, None, 2048)
+        assert np.array_equal(t, np.tile(np.arange(2048, dtype=np.int32), (R, 1)))
+        pos = np.full(R, Lk - 3, np.int32)
+        assert np.array_equal(run(s, pos, 2048), oracle.topk(s, pos, 2048))
+
+
 @pytest.mark.parametrize("R,Lk", [(32, 200000), (3, 70001), (100, 16384), (1, 1000000)])
 def test_split_rows(R, Lk):
     """Few long rows: the split path (bounds per split, candidate collection, per-row select)."""
