@@ -19,10 +19,19 @@ def _bf16_np(x: torch.Tensor) -> np.ndarray:
     return oracle.bf16_bits_to_f64(raw(x))
 
 
-def run_and_compare(B, Lq, Lk, Hq, Dqk, Dv, k, t_kind="random", seed=0):
+def run_and_compare(B, Lq, Lk, Hq, Dqk, Dv, k, t_kind="random", seed=0, rope_growth=0.0):
     g = torch.Generator(device=DEV).manual_seed(seed)
     q = torch.randn(B, Lq, Hq, Dqk, generator=g, device=DEV).to(torch.bfloat16)
-    kv = torch.randn(B, Lk, Dqk, generator=g, device=DEV).to(torch.bfloat16)
+    kv = torch.randn(B, Lk, Dqk, generator=g, device=DEV)
+    if rope_growth:
+        # the key-only columns of row s scaled by 1 + rope_growth * s / Lk: with
+        # T in ascending order the logits keep growing along the index set.  The
+        # softmax then rests on a few rows, so the output is about one value row:
+        # values are scaled by 1/4 to keep it below about 1.5, where one bf16 ulp
+        # (2^-7 at most) stays below the 2e-2 max-abs bound
+        kv[:, :, Dv:] *= 1.0 + rope_growth * torch.arange(Lk, device=DEV, dtype=torch.float32)[None, :, None] / Lk
+        kv[:, :, :Dv] *= 0.25
+    kv = kv.to(torch.bfloat16)
     rng = np.random.default_rng(seed)
     t = np.full((B, Lq, k), -1, np.int32)
     for b in range(B):
@@ -34,6 +43,9 @@ def run_and_compare(B, Lq, Lk, Hq, Dqk, Dv, k, t_kind="random", seed=0):
             elif t_kind == "full":
                 n = min(k, Lk)
                 t[b, i, :n] = rng.choice(Lk, size=n, replace=False)
+            elif t_kind == "sorted":
+                n = min(k, Lk)
+                t[b, i, :n] = np.sort(rng.choice(Lk, size=n, replace=False))
             elif t_kind == "dup":
                 t[b, i] = rng.integers(0, min(Lk, k // 4 + 1), size=k)
             elif t_kind == "beyond":
@@ -98,6 +110,18 @@ def test_mla_wide_full_index_sets():
 def test_mla_wide_repeated_indices():
     # each occurrence of an index is one more term of the softmax
     run_and_compare(1, 2, 3000, 64, 576, 512, 512, t_kind="dup", seed=12)
+
+
+@pytest.mark.parametrize("B,Lq,k", [
+    (1, 2, 2048),     # decode shape: 16 chunks per (query, 64 heads) and the merge
+    (1, 300, 1024),   # one chunk per query, 32 tiles in one workgroup
+])
+def test_mla_wide_growing_logits(B, Lq, k):
+    """Logits that keep growing along the (ascending) index set: the softmax
+    reference is raised many times in the middle of a sweep (each raise by more
+    than 2^8), so the rescale of the accumulated output and row sums runs
+    repeatedly."""
+    run_and_compare(B, Lq, 4000, 64, 576, 512, k, t_kind="sorted", seed=21 + Lq, rope_growth=200.0)
 
 
 def test_mla_wide_empty_index_set():
