@@ -37,9 +37,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Order-preserving 32-bit key of a score: larger key <=> larger float,
 // with -0 and +0 mapped to the same key.  NaN is outside the contract.
 __device__ __forceinline__ uint32_t score_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u << 1) == 0u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f + 0.0f);   // -0 + 0 = +0; exact otherwise (denormals kept)
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

@@ -727,7 +727,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     constexpr bool kPipe = kMfma32 && sizeof(IdxT) == 2;
     const int waves = p.nthreads / kWave;
     const int R = waves * TW;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, g = lane >> 4, n = lane & 15;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave, g = lane >> 4,
+              n = lane & 15;
 
     extern __shared__ __align__(16) unsigned char smem[];
     const PrefillLds L = prefill_lds(waves, TW, S::PITCH, p.cap, (int)sizeof(IdxT), kStaged ? 1 : kPipe ? 2 : 0);
@@ -877,7 +878,9 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         const int pos = off + i;
         if (i >= Lq || base > pos) return false;
         const int s = base + lane;
-        if (p.scores && s < Lk) p.scores[(row0 + i) * Lk + s] = s <= pos ? sc : -INFINITY;
+        if (p.scores) {   // the full score row, for tests only
+            if (s < Lk) p.scores[(row0 + i) * Lk + s] = s <= pos ? sc : -INFINITY;
+        }
         const bool cand = s <= pos && sc > st.thr_f;
         const uint64_t m = ballot(cand);
         if (m) {
@@ -899,7 +902,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // does every row past a quarter of its slack.
     auto raise_flags = [&](int it, bool need) {
         if constexpr (kBinned) {
-            if (need && lane == 0) atomicOr(&flags[it % 3], 1);
+            if (need && lane == 0) flags[it % 3] = 1;   // the words are only tested for nonzero
             if (wave == 0 && lane == 0) flags[(it + 1) % 3] = 0;
         }
     };
@@ -1056,7 +1059,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             __builtin_amdgcn_sched_barrier(0);
             // block blk-1's selection (none before block 0: a base past every position)
             const float lin_prev = linbuf[(PAR ^ 1) * (8 * KB) + lin_get];
-            const bool need = select_binned(combine(p0_prev, p1) + lin_prev, blk >= 1 ? bmap(blk - 1) * KB : INT_MAX);
+            const bool need = select_binned(combine(p0_prev, p1) + lin_prev, blk >= 1 ? bmap(blk - 1) * KB : Lk);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rf = 0; rf < 2; ++rf) a1[rf] = mfma_fp8_32x32x64(Q32f.a[rf][0], B[1][0], z);
