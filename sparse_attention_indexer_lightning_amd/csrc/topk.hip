@@ -58,7 +58,7 @@ struct TopkShared {
 template <typename Get, typename Idx>
 __device__ void ordered_output(TopkShared &sh, int n, uint32_t theta, int need_eq, int k, Get get, Idx idx,
                                int32_t *out) {
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     uint32_t gt_base = 0, eq_base = 0;
     int par = 0;
     for (int c0 = 0; c0 < n; c0 += kThreads, par ^= 1) {
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void row_topk_kernel(TopkArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     TopkShared &sh = *reinterpret_cast<TopkShared *>(smem_raw);
     const int r = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     int pos;
     if (a.pos_Lq > 0) pos = a.Lk - a.pos_Lq + r % a.pos_Lq;
     else pos = a.row_pos ? a.row_pos[r] : a.Lk - 1;
@@ -266,7 +266,8 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_bound(TopkArgs a, Sp
 // (ballot + lane prefix per 64 keys): no block-wide ordering, so no barriers.
 // The regions of a row, in (split, wavefront) order, are in index order.
 __global__ __launch_bounds__(kSplitThreads) void topk_split_collect(TopkArgs a, SplitPlan pl, SplitWs ws) {
-    const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave),
+              lane = tid % kWave;
     const int n = row_valid(a, r);
     const int q = pl.N / kRegions;
     const int j0 = s * pl.N + wave * q, j1 = min(j0 + q, n);
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void topk_split_select(TopkArgs a, SplitP
     const int nreg = pl.S * kRegions;
     const int q = pl.N / kRegions;
     {
-        const int wave = tid / kWave, lane = tid % kWave;
+        const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
         const int i0 = 2 * tid;
         const int c0 = i0 < nreg ? ws.count[(size_t)r * nreg + i0] : 0;
         const int c1 = i0 + 1 < nreg ? ws.count[(size_t)r * nreg + i0 + 1] : 0;
