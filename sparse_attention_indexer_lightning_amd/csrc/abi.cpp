@@ -223,7 +223,7 @@ idxc_indexer_desc paged_as_dense(const idxc_paged_indexer_desc *d);
 
 // Two ways to score a serving batch, chosen from the descriptor alone:
 //  * fused: the prefill kernel with page lookups per 64-key block scores and
-//    selects every row without storing scores (one workgroup per 8 rows of
+//    selects every row without storing scores (one workgroup per 4-8 rows of
 //    a sequence, so it pays off when the batch holds prefill chunks: more
 //    than 4 rows per sequence on average, fp8 with 64 heads of 128);
 //  * split: every row's keys split over many workgroups into score rows of
