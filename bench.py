@@ -15,6 +15,10 @@ per second; plus the gather bandwidth of sparse MLA.
 is algorithmic flops (pairs x H x D x 2) over the average launch time measured
 with HIP events on the launch stream.  ``traffic`` comes from rocprofv3 counter
 runs committed under profiles/ (null when not measured for this kernel build).
+``operand_peak`` is the rate of plain dense MFMA chains on this workload's own
+operand bytes: the engine clock falls when MFMA operands toggle, so random
+operands cap an MFMA-bound kernel below the published ``peak``.  The retention
+sweep reports the sparse MLA prefill layer the same way (bf16).
 
 ``cpu_baseline``: the plain fp64 CPU oracle on a bounded seeded sample of query
 rows of the same workload, in the same unit.
@@ -32,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_prefill_64k_traffic.json")
 
@@ -89,7 +94,42 @@ def headline(args, torch, sa, inputs):
     ms = time_steps(step, args.steps, args.warmup, torch)
     pairs = causal_pairs(wl.Lq, wl.Lk, wl.B)
     flops = pairs * wl.H * wl.D * 2
-    return wl, ms, pairs, flops, t_cache
+    peak_ops = operand_peak(torch, sa, 0, q, k)
+    return wl, ms, pairs, flops, t_cache, peak_ops
+
+
+def operand_peak(torch, sa, kind, a, b):
+    """TFLOP/s of a plain chain of dense MFMAs (idxc_calib_mfma_rate) whose
+    operands are bytes of the tensors a and b: on this part the engine clock
+    falls when MFMA operands toggle, so random operands cap an MFMA-bound
+    kernel below the published peak.  kind 0: fp8 32x32x64, 1: bf16 32x32x16."""
+    import ctypes
+    L = sa.lib()
+    f = L.idxc_calib_mfma_rate
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 512                                  # four wavefronts each: two per SIMD
+    iters = 6000 if kind == 0 else 12000          # about 6-7 ms per launch
+    flop = (2 * 32 * 32 * 64 if kind == 0 else 2 * 32 * 32 * 16) * 16 * iters * blocks * 4
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=a.device)
+    s = torch.cuda.current_stream()
+
+    def launch():
+        rc = f(kind, a.data_ptr(), a.numel() * a.element_size(), b.data_ptr(), b.numel() * b.element_size(), iters,
+               blocks, out.data_ptr(), s.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"idxc_calib_mfma_rate failed: {rc}")
+
+    launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(3):
+        launch()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return flop * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def decode(args, torch, sa, inputs):
@@ -293,6 +333,9 @@ def retention_sweep(args, torch, sa, inputs):
                      "stack_ms": round(timed(lambda: st.run(pat)), 3),
                      "modelled_stack_ms": round(nf * t_idx + n_layers * (t_att + t_ffn), 3),
                      "indexer_ms": round(nf * t_idx, 3), "indexer_saved_ms": round((n_layers - nf) * t_idx, 3)}
+    mla_flops = wl.B * wl.Lq * wl.Hq * wl.topk * (wl.Dqk + wl.Dv) * 2
+    mla_tflops = mla_flops / (t_att * 1e-3) / 1e12
+    mla_peak = operand_peak(torch, sa, 1, s0["q"], s0["kv"])
     full = res["1/1"]["stack_ms"]
     for r in res.values():
         r["speedup_vs_all_full"] = round(full / r["stack_ms"], 4)
@@ -301,7 +344,13 @@ def retention_sweep(args, torch, sa, inputs):
     torch.cuda.empty_cache()
     return {"workload": "stack_32k", "L": wl.Lq, "layers": n_layers, "input_sets": n_sets,
             "indexer_ms_per_full_layer": round(t_idx, 3), "sparse_mla_ms_per_layer": round(t_att, 3),
-            "ffn_and_residual_ms_per_layer": round(t_ffn, 3), "patterns": res,
+            "ffn_and_residual_ms_per_layer": round(t_ffn, 3),
+            "sparse_mla_roofline": {"bound": "mfma", "achieved": round(mla_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(mla_tflops / PEAK_BF16_TFLOPS, 4),
+                                    "operand_peak": round(mla_peak, 1),
+                                    "frac_of_operand_peak": round(mla_tflops / mla_peak, 4),
+                                    "flops_per_layer": mla_flops},
+            "patterns": res,
             "note": "stack_ms: the whole 16-layer stack timed end to end (X chained, layer l on input set l mod 4); "
                     "modelled_stack_ms = Full layers x indexer + all layers x (sparse MLA + FFN stand-in)"}
 
@@ -474,7 +523,7 @@ def main():
     if args.profile:
         profile_run(args, torch, sa, inputs)
         return
-    wl, ms, pairs, flops, t_head = headline(args, torch, sa, inputs)
+    wl, ms, pairs, flops, t_head, peak_ops = headline(args, torch, sa, inputs)
     if args.profile_only:
         print(json.dumps({"ms_per_step": ms}))
         return
@@ -499,7 +548,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                      "kernel": "prefill_kernel<FP8,128,64,u16>",
-                     "flops_per_launch": flops},
+                     "flops_per_launch": flops,
+                     "operand_peak": round(peak_ops, 1), "frac_of_operand_peak": round(achieved / peak_ops, 4),
+                     "operand_peak_note": "fp8 32x32x64 MFMA chains on this workload's q and k bytes (engine "
+                                          "clock falls with operand toggling); peak stays the published one"},
     }
     if not args.no_decode:
         line["secondary"] = decode(args, torch, sa, inputs)

@@ -5,6 +5,7 @@ Pointers passed here are fake, 16-byte-aligned addresses: each call below must
 fail validation, which happens before anything is enqueued.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -14,6 +15,7 @@ import sparse_attention_indexer_lightning_amd as sa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "idxcache.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, PATTERN, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -9
 BF16, FP8, FP32 = 1, 2, 3
@@ -22,14 +24,17 @@ FAKE_ODD = ctypes.c_void_p(0x10008)   # 8-byte aligned only
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:idxc_status|const char \*|int)\s+(\w+)\s*\(", src, re.M)))
+    names = set()
+    for h in HEADERS:
+        src = open(h).read()
+        names |= set(re.findall(r"^(?:idxc_status|const char \*|int)\s+(\w+)\s*\(", src, re.M))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
     L = sa.lib()
     names = declared_functions()
-    assert {"idx_score_topk", "idx_topk", "idx_cache_route", "sparse_mla_attn"} <= set(names)
+    assert {"idx_score_topk", "idx_topk", "idx_cache_route", "sparse_mla_attn", "idxc_calib_mfma_rate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert L.idxc_abi_version() == 1
@@ -467,3 +472,18 @@ def test_paged_workspace_by_mode():
     bf16 = paged_ws(num_seqs=4, total_q=4800, max_seq_len=20000, num_blocks=4000, block_size=64, max_blocks=400,
                     qd=BF16, kd=BF16, wd=FP32, D=64)
     assert bf16 >= 4800 * 20000 * 4    # the fused paged form is fp8-only: split path
+
+
+def test_calib_rejects_before_launch():
+    L = sa.lib()
+    f = L.idxc_calib_mfma_rate
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(0, None, 64, FAKE, 64, 1, 1, FAKE, None) == NULL
+    assert f(0, FAKE, 64, FAKE, 64, 1, 1, None, None) == NULL
+    assert f(0, FAKE, 8, FAKE, 64, 1, 1, FAKE, None) == SHAPE
+    assert f(1, FAKE, 64, FAKE, 64, 0, 1, FAKE, None) == SHAPE
+    assert f(1, FAKE, 64, FAKE, 64, 1, 0, FAKE, None) == SHAPE
+    assert f(0, FAKE_ODD, 64, FAKE, 64, 1, 1, FAKE, None) == ALIGN
+    assert f(2, FAKE, 64, FAKE, 64, 1, 1, FAKE, None) == DTYPE
