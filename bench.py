@@ -446,6 +446,38 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def sa_scores_rows(torch, inputs, wl, rows):
+    """The fused kernel's fp32 scores of the listed rows of prefill_64k (its
+    test-only full score output, written once outside any timed region)."""
+    import sparse_attention_indexer_lightning_amd as sa
+    q, k, w = inputs.indexer_inputs(wl, 0, "cuda:0")
+    scores = torch.empty(wl.B, wl.Lq, wl.Lk, dtype=torch.float32, device="cuda:0")
+    sa.idx_score_topk(q, k, w, wl.topk, scores_dbg=scores)
+    torch.cuda.synchronize()
+    out = scores[0][torch.from_numpy(rows).to(scores.device)].cpu().numpy()
+    del scores, q, k, w
+    torch.cuda.empty_cache()
+    return out
+
+
+def _score_error(torch, g_rows, sampled):
+    """Largest score difference over the sampled rows, as a fraction of
+    |oracle| + 0.01 * max|oracle row| (the GPU tests allow 1e-2 for fp8)."""
+    import numpy as np
+    s_or = np.concatenate([s for _, _, s in sampled])
+    worst, worst_abs = 0.0, 0.0
+    for g, o in zip(g_rows, s_or):
+        fin = np.isfinite(o)
+        if not fin.any():
+            continue
+        scale = np.abs(o[fin]).max()
+        err = np.abs(g[fin].astype(np.float64) - o[fin])
+        worst = max(worst, float((err / (np.abs(o[fin]) + 0.01 * scale)).max()))
+        worst_abs = max(worst_abs, float(err.max()))
+    return {"max_err_over_scale": float(f"{worst:.3g}"), "max_abs": float(f"{worst_abs:.3g}"),
+            "scale": "|oracle| + 0.01 max|oracle row|; tolerance of the GPU tests 1e-2"}
+
+
 def cpu_baseline(args, inputs, torch, t_gpu=None):
     """Oracle pairs/s on the host (bounded seeded row sample of prefill_64k):
     once on the CPU share this process is given (OMP_NUM_THREADS, else every
@@ -475,9 +507,10 @@ def cpu_baseline(args, inputs, torch, t_gpu=None):
         while wall < seconds and start + done_rows < wl.Lq:
             rows = np.sort(order[start + done_rows:start + done_rows + batch]).astype(np.int64)
             t0 = time.perf_counter()
-            t_or, _ = oracle.indexer_topk(qr, kr, wr, ("fp8", "fp8", "bf16"), wl.topk, rows=rows, nthreads=nthreads)
+            t_or, s_or = oracle.indexer_topk(qr, kr, wr, ("fp8", "fp8", "bf16"), wl.topk, rows=rows,
+                                             nthreads=nthreads)
             wall += time.perf_counter() - t0
-            sampled.append((rows, t_or))
+            sampled.append((rows, t_or, s_or))
             done_rows += rows.size
             done_pairs += int((rows + 1).sum())
         return done_rows, done_pairs, wall
@@ -486,8 +519,8 @@ def cpu_baseline(args, inputs, torch, t_gpu=None):
     rows_1, pairs_1, wall_1 = run(1, args.cpu_seconds / 3, rows_n)
     agreement = None
     if t_gpu is not None:
-        rows = np.concatenate([r for r, _ in sampled])
-        t_or = np.concatenate([t for _, t in sampled])
+        rows = np.concatenate([r for r, _, _ in sampled])
+        t_or = np.concatenate([t for _, t, _ in sampled])
         t_g = t_gpu.reshape(-1, wl.topk)[torch.from_numpy(rows).to(t_gpu.device)].cpu().numpy()
         share = []
         for a, b in zip(t_g, t_or):
@@ -496,7 +529,8 @@ def cpu_baseline(args, inputs, torch, t_gpu=None):
         share = np.asarray(share)
         agreement = {"rows": int(rows.size), "overlap_mean": round(float(share.mean()), 6),
                      "overlap_min": round(float(share.min()), 6),
-                     "rows_identical": int(sum(np.array_equal(a, b) for a, b in zip(t_g, t_or)))}
+                     "rows_identical": int(sum(np.array_equal(a, b) for a, b in zip(t_g, t_or))),
+                     "score_error": _score_error(torch, sa_scores_rows(torch, inputs, wl, rows), sampled)}
     return {"value": round(pairs_n / wall_n, 1), "unit": "pairs/s", "cores": threads, "kind": "oracle",
             "t_agreement_with_gpu": agreement,
             "sample": f"{rows_n} seeded random query rows of prefill_64k ({pairs_n} causal pairs, fp64 scores + "
