@@ -70,6 +70,12 @@ static_assert(kPipeWaves == 4 || kPipeWaves == 8, "the linear-term MFMA covers r
 constexpr int kChunkMax = 4;    // 16-byte chunks each thread stages per key block
 constexpr int kPadEntries = 256; // candidate-buffer padding read by 4-per-lane passes
 constexpr int kHistWords = 320;  // 256 bins + one dummy slot per lane for masked-off updates
+// The pipelined sweep keeps 16-bit candidate indices also for keys beyond
+// 65536: a row's candidates are in index order, so segment j of the keys
+// (j * 65536 ..) starts at a buffer position recorded per row (kMaxSeg
+// segments, keys up to kMaxSeg * 65536), and an index is its low 16 bits plus
+// the segment of its position.
+constexpr int kMaxSeg = 16;
 // Sampled starting threshold of the 64-head sweep: every kSampleStride-th key
 // block is scored first; a row's threshold is then its sample's r-th largest
 // key, r = ceil(7/4 * k * (sampled keys) / (keys)), unless r is below
@@ -530,13 +536,42 @@ __device__ int filter_gt(uint32_t *bk, IdxT *bi, int cnt, uint32_t gt, uint32_t 
     return out;
 }
 
+// Segment starts after an in-place stable filter of bkey[0..cnt) that keeps
+// entry i iff key_i > gt, or key_i == eq and it is among the first eq_keep
+// such entries: segs[j] (j = 1 .. nseg-1, a start position or INT_MAX when the
+// segment has not been reached) becomes the number of kept entries before it.
+// Reads the keys, so it runs before the filter.  Wave-level.
+__device__ void seg_remap(const uint32_t *bkey, int cnt, int *segs, int nseg, uint32_t gt, uint32_t eq, int eq_keep,
+                          int lane) {
+    for (int j = 1; j < nseg; ++j) {
+        const int pj = segs[j];
+        if (pj == INT_MAX) break;   // later segments not reached either
+        const int lim = min(pj, cnt);
+        int ngt = 0, neq = 0;
+        for (int base = 0; base < lim; base += kStep) {
+            const int e0 = base + 4 * lane;
+            const v4u kk = *reinterpret_cast<const v4u *>(bkey + e0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bool in = e0 + t < lim;
+                ngt += __popcll(ballot(in && kk[t] > gt));
+                neq += __popcll(ballot(in && kk[t] == eq));
+            }
+        }
+        const int np = ngt + min(neq, eq_keep);
+        wave_lds_order();
+        if (lane == 0) segs[j] = np;
+        wave_lds_order();
+    }
+}
+
 // Exact k-th largest key among bkey[0..cnt) (cnt >= k) by MSB-first radix
 // select, then in-place stable compaction to the k best (ties: lowest index =
 // earliest entry).  Wave-level; `hist` is this wave's 256-entry LDS scratch.
 // Returns the k-th largest key.
 template <typename IdxT>
 __device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, uint32_t *hist, int lane,
-                                   uint32_t *kept_max = nullptr) {
+                                   uint32_t *kept_max = nullptr, int *segs = nullptr, int nseg = 1) {
     // bits above `top` are common to every key (from the buffer's min and max)
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
     for (int base = 0; base < cnt; base += kStep) {
@@ -577,6 +612,7 @@ __device__ uint32_t select_compact(uint32_t *bkey, IdxT *bidx, int &cnt, int k, 
         top = shift;
         wave_lds_order();
     }
+    if (nseg > 1) seg_remap(bkey, cnt, segs, nseg, prefix, prefix, need, lane);
     cnt = filter4<true, IdxT>(bkey, bidx, cnt, prefix, prefix, need, lane, kept_max);
     return prefix;
 }
@@ -592,6 +628,7 @@ struct BinState {
     uint32_t thr;     // append filter: key > thr
     float thr_f;      // the same filter on scores: score > thr_f
     uint32_t lo;      // histogram base (<= every buffered key)
+    int cur_seg;      // key segment of the last append (segment table)
 };
 
 // Largest float whose order-preserving key is <= thr: for every finite f,
@@ -650,8 +687,9 @@ __device__ uint32_t buffer_min(const uint32_t *bkey, int cnt, int lane) {
 }
 
 template <typename IdxT>
-__device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, uint32_t *hist, int lane) {
-    const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane);
+__device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, uint32_t *hist, int lane, int *segs,
+                              int nseg) {
+    const uint32_t theta = select_compact<IdxT>(bkey, bidx, st.cnt, k, hist, lane, nullptr, segs, nseg);
     st.thr = theta;
     st.thr_f = key_floor_float(theta);
 }
@@ -665,7 +703,7 @@ __device__ void compact_exact(uint32_t *bkey, IdxT *bidx, BinState &st, int k, u
 // Precondition: st.cnt >= k.
 template <typename IdxT>
 __device__ __forceinline__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinState &st, int k, int cap, uint32_t *hist,
-                               uint32_t *pad_k, IdxT *pad_i, int lane) {
+                               uint32_t *pad_k, IdxT *pad_i, int lane, int *segs, int nseg) {
     rebuild_hist<IdxT>(bkey, st, buffer_min<IdxT>(bkey, st.cnt, lane), hist, lane);
     int bstar;
     uint32_t above;
@@ -674,12 +712,13 @@ __device__ __forceinline__ void compact_binned(uint32_t *bkey, IdxT *bidx, BinSt
     wave_lds_order();
     if (bstar > 0 && (int)nkeep <= cap - 2 * KB) {
         const uint32_t edge = st.lo + bin_floor(bstar);   // keep keys >= edge
+        if (nseg > 1) seg_remap(bkey, st.cnt, segs, nseg, edge - 1u, 0u, 0, lane);
         st.cnt = filter_gt<IdxT>(bkey, bidx, st.cnt, edge - 1u, pad_k, pad_i, lane);
         st.thr = edge - 1u;
         st.thr_f = key_floor_float(st.thr);
         return;
     }
-    compact_exact<IdxT>(bkey, bidx, st, k, hist, lane);
+    compact_exact<IdxT>(bkey, bidx, st, k, hist, lane, segs, nseg);
 }
 
 struct PrefillParams {
@@ -702,7 +741,7 @@ struct PrefillParams {
 
 // LDS plan of the prefill kernel; identical on host and device.
 struct PrefillLds {
-    size_t ktile, stage, hist, flags, state, bkey, bidx, total;
+    size_t ktile, stage, hist, flags, state, segs, bkey, bidx, total;
 };
 
 // `stage` holds one score per (row, key of a block): once for the staged
@@ -722,6 +761,8 @@ __host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, 
     off += 64;
     L.state = off;
     off += (size_t)R * 8;
+    L.segs = off;
+    off += (size_t)waves * kMaxSeg * 4;
     L.bkey = off;
     off += ((size_t)R * cap + kPadEntries) * 4;
     off = (off + 15) & ~(size_t)15;
@@ -739,7 +780,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     constexpr bool kBinned = TW == 1;       // binned selection + batched compaction
     constexpr bool kMfma32 = E == Enc::FP8 && H == 64 && D == 128;
     // the pipelined sweep below needs kPipeWaves wavefronts, which the LDS
-    // plan always gives with 16-bit candidate indices (keys up to 65536)
+    // plan always gives with 16-bit candidate indices (keys up to 65536, or up
+    // to kMaxSeg * 65536 with the segment table)
     constexpr bool kPipe = kMfma32 && sizeof(IdxT) == 2;
     const int waves = p.nthreads / kWave;
     const int R = waves * TW;
@@ -848,8 +890,20 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
     if (tid < 4) flags[tid] = 0;   // words 0-2: compaction requests; word 3: the sample failed
     BinState st;
-    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u;
+    st.cnt = 0; st.thr = 0u; st.thr_f = -INFINITY; st.lo = 0u; st.cur_seg = 0;
     const int want_level = p.topk + (p.cap - p.topk) / 4;   // past a quarter of the slack
+    // segment table of this wave's row (pipelined sweep with keys beyond 65536)
+    int *segs = reinterpret_cast<int *>(smem + L.segs) + wave * kMaxSeg;
+    const int nseg = kPipe ? (Lk + 65535) >> 16 : 1;
+    auto seg_reset = [&]() {   // an empty buffer: every segment not reached yet
+        if (nseg > 1) {
+            wave_lds_order();
+            if (lane < kMaxSeg) segs[lane] = lane == 0 ? 0 : INT_MAX;
+            wave_lds_order();
+        }
+        st.cur_seg = 0;
+    };
+    seg_reset();
 
     // stage key block 0.  Thread tid stages 16-byte chunks tid + c*blockDim
     // (c < cpt).  Keys past Lk are clamped to the last key: their scores lie
@@ -903,6 +957,17 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         if (m) {
             uint32_t *bk = bkey_all + (size_t)wave * p.cap;
             IdxT *bi = bidx_all + (size_t)wave * p.cap;
+            if (nseg > 1) {
+                // the first append in a later key segment starts it (blocks of
+                // 64 keys never straddle a segment; appends come in index order)
+                const int sg = base >> 16;
+                if (sg > st.cur_seg) {
+                    wave_lds_order();
+                    if (lane > st.cur_seg && lane <= sg) segs[lane] = st.cnt;
+                    wave_lds_order();
+                    st.cur_seg = sg;
+                }
+            }
             const int at = st.cnt + lanes_below(m);
             const uint32_t key = score_key(sc);
             if (cand) {
@@ -927,7 +992,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         if constexpr (kBinned) {
             if (st.cnt > want_level && flags[it % 3]) {
                 compact_binned<IdxT>(bkey_all + (size_t)wave * p.cap, bidx_all + (size_t)wave * p.cap, st, p.topk,
-                                     p.cap, hist, bkey_all + (size_t)R * p.cap, bidx_all + (size_t)R * p.cap, lane);
+                                     p.cap, hist, bkey_all + (size_t)R * p.cap, bidx_all + (size_t)R * p.cap, lane, segs,
+                                     nseg);
             }
         }
     };
@@ -984,8 +1050,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         auto fetch1c = [&](int blk, int kr) {
             const int key = min(blk * KB + kr, Lk - 1);   // past Lk: clamped, never used
             // 32-bit offset from the sequence's base, or from the block's page
-            // (this sweep runs with 16-bit key indices, so at most 65536 keys
-            // of 128 bytes): one VALU add instead of 64-bit address arithmetic
+            // (this sweep covers at most kMaxSeg * 65536 keys of 128 bytes,
+            // under 2^28 bytes): one VALU add instead of 64-bit address arithmetic
             if constexpr (Paged) {
                 const unsigned char *pb = page_of(min(blk * KB, Lk - 1));
                 const uint32_t o = (uint32_t)(key & ((1 << p.bs_log2) - 1)) * (uint32_t)S::ROWB + (uint32_t)kcol;
@@ -1057,6 +1123,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             st.thr = thr;
             st.thr_f = key_floor_float(thr);
             st.lo = 0u;
+            seg_reset();
         };
         for (;;) {
         const int niter = ns + nblk;
@@ -1157,6 +1224,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         st.thr = 0u;
         st.thr_f = -INFINITY;
         st.lo = 0u;
+        seg_reset();
         ns = 0;
         __syncthreads();
         }
@@ -1301,9 +1369,20 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         uint32_t *bk = bkey_all + (size_t)row * p.cap;
         IdxT *bi = bidx_all + (size_t)row * p.cap;
         int cnt = kBinned ? st.cnt : rcnt[row];
-        if (cnt > p.topk) (void)select_compact<IdxT>(bk, bi, cnt, p.topk, hist, lane);
+        if (cnt > p.topk) (void)select_compact<IdxT>(bk, bi, cnt, p.topk, hist, lane, nullptr, segs, nseg);
         int32_t *o = p.t_out + (row0 + i) * p.topk;
-        for (int j = lane; j < p.topk; j += kWave) o[j] = j < cnt ? (int32_t)bi[j] : -1;
+        for (int j = lane; j < p.topk; j += kWave) {
+            int32_t v = -1;
+            if (j < cnt) {
+                v = (int32_t)bi[j];
+                if (nseg > 1) {   // the index's segment: the last one starting at or before j
+                    int sg = 0;
+                    for (int b = 1; b < nseg; ++b) sg += segs[b] <= j ? 1 : 0;
+                    v |= sg << 16;
+                }
+            }
+            o[j] = v;
+        }
         if (p.scores) {
             const int pos = off + i;
             for (int s = (pos / KB + 1) * KB + lane; s < Lk; s += kWave)
@@ -1572,8 +1651,11 @@ PrefillPlan plan_prefill(const IndexerArgs &a) {
     const int rowb = a.D * eb, pitch = rowb + 16;
     const int tw = 64 / a.H;
     const bool staged = a.H < 16;
-    pl.idx_bytes = a.Lk <= 65536 ? 2 : 4;
-    const bool pipe = a.qk_enc == Enc::FP8 && a.H == 64 && a.D == 128 && pl.idx_bytes == 2;
+    // 16-bit candidate indices: keys up to 65536, or (pipelined 64-head fp8
+    // sweep, with its segment table) up to kMaxSeg * 65536
+    const bool mfma32 = a.qk_enc == Enc::FP8 && a.H == 64 && a.D == 128;
+    pl.idx_bytes = a.Lk <= 65536 || (mfma32 && (long long)a.Lk <= (long long)kMaxSeg * 65536) ? 2 : 4;
+    const bool pipe = mfma32 && pl.idx_bytes == 2;
     const int stage_bufs = staged ? 1 : pipe ? 2 : 0;
     const int nchunk = KB * rowb / 16;
     int min_waves = (nchunk + kChunkMax * kWave - 1) / (kChunkMax * kWave);

@@ -104,7 +104,8 @@ def test_edge_shapes_fp8(B, Lq, Lk, topk):
 
 
 def test_long_context_32bit_indices():
-    """Lk > 65536 switches the candidate buffers to 32-bit indices."""
+    """Lk > 65536: the fused kernel keeps 16-bit candidate indices with a
+    per-row table of where each 65,536-key segment starts in the buffer."""
     wl = inputs.Workload("l", 1, 40, 70000, 64, 128, 2048, "fp8", "bf16", 6)
     q, k, w = inputs.indexer_inputs(wl, 0, DEV)
     t, scores = run_full(q, k, w, 2048)
@@ -218,3 +219,35 @@ def test_sampled_threshold_closed_forms(kind):
     t, _ = run_full(q, kk, w, k)
     tg = t.cpu().numpy().reshape(Lq, k)
     assert np.array_equal(tg, np.tile(np.arange(k, dtype=np.int32), (Lq, 1))), kind
+
+
+def test_long_context_segments_vs_oracle():
+    """Four key segments (Lk = 200,000): sampled rows against the oracle."""
+    Lq, Lk = 48, 200000
+    wl = inputs.Workload("s", 1, Lq, Lk, 64, 128, 2048, "fp8", "bf16", 9)
+    q, k, w = inputs.indexer_inputs(wl, 0, DEV)
+    t, scores = run_full(q, k, w, 2048)
+    rows = np.array([0, 21, 47], dtype=np.int64)
+    to, so = indexer_oracle(q, k, w, 2048, rows=rows)
+    sg = scores.cpu().numpy().reshape(Lq, -1)[rows]
+    check_scores(sg, so, RTOL["fp8"], "Lk=200000")
+    pos = oracle.row_positions(1, Lq, Lk, rows)
+    check_index_sets(t.cpu().numpy().reshape(Lq, -1)[rows], to, so, pos, 2048, RTOL["fp8"], "Lk=200000")
+
+
+@pytest.mark.parametrize("kind", ["recency", "reverse", "ties"])
+def test_long_context_segments_closed_forms(kind):
+    """Closed forms over three key segments: I = s puts every selected key in
+    the last segment (the earlier ones end up empty), I = -s and all-equal
+    scores keep every selected key in the first (later segments never
+    reached); T is known exactly."""
+    Lq, Lk, k = 8, 140000, 2048
+    q, kk, w = inputs.closed_form_indexer(1, Lk, 64, 128, "fp8", kind, device=DEV)
+    q = q[:, Lk - Lq:].contiguous()
+    w = w[:, Lk - Lq:].contiguous()
+    t, _ = run_full(q, kk, w, k, dbg=False)
+    tg = t.cpu().numpy().reshape(Lq, k)
+    for i in range(Lq):
+        pos = Lk - Lq + i
+        want = np.arange(pos - k + 1, pos + 1, dtype=np.int32) if kind == "recency" else np.arange(k, dtype=np.int32)
+        assert np.array_equal(tg[i], want), (kind, i)
