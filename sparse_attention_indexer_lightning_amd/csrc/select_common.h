@@ -33,6 +33,8 @@ __device__ __forceinline__ void keep_top4(uint32_t (&top)[kLocal], uint32_t u) {
 template <int NT, typename Sh, typename Get>
 __device__ uint32_t block_select(Sh &sh, int n, int need, Get get, uint32_t *above_out) {
     constexpr int NW = NT / kWave;
+    constexpr int BPT = kBins / NT;            // histogram bins per thread
+    static_assert(BPT == 2 || (BPT % 4 == 0 && BPT > 0), "bins per thread: 2 or a multiple of 4");
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
     for (int i = tid; i < n; i += NT) {
@@ -62,28 +64,52 @@ __device__ uint32_t block_select(Sh &sh, int n, int need, Get get, uint32_t *abo
             if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & dmask], 1u);
         }
         __syncthreads();
-        // suffix scan over kBins bins: lane l of wave 0 owns bins [32l, 32l+32)
-        if (wave == 0) {
-            uint32_t sum = 0;
-            for (int j = 0; j < kBins / kWave; ++j) sum += sh.hist[(kBins / kWave) * lane + j];
-            uint32_t S = sum;
+        // Suffix sums over the bins, highest first.  Thread t owns the BPT
+        // consecutive bins [BPT t, BPT t + BPT) (one 8- or 16-byte LDS read
+        // each); a wavefront scan and the wavefront totals give every thread
+        // S = the keys in its bins and above, and the one thread whose bins
+        // hold the need-th largest key picks the bin.
+        uint32_t h[BPT];
+        if constexpr (BPT == 2) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(&sh.hist[2 * tid]);
+            h[0] = v.x;
+            h[1] = v.y;
+        } else {
 #pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t v = __shfl_down(S, o, kWave);
-                if (lane + o < kWave) S += v;
+            for (int j = 0; j < BPT; j += 4) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(&sh.hist[BPT * tid + j]);
+                h[j] = v.x;
+                h[j + 1] = v.y;
+                h[j + 2] = v.z;
+                h[j + 3] = v.w;
             }
-            const uint32_t E = S - sum;
-            if (E < (uint32_t)need && S >= (uint32_t)need) {
-                uint32_t c = E;
-                int bsel = 0;
-                for (int j = kBins / kWave - 1; j >= 0; --j) {
-                    const uint32_t h = sh.hist[(kBins / kWave) * lane + j];
-                    if (c + h >= (uint32_t)need) { bsel = j; break; }
-                    c += h;
+        }
+        uint32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) sum += h[j];
+        uint32_t S = sum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t v = __shfl_down(S, o, kWave);
+            if (lane + o < kWave) S += v;
+        }
+        if (lane == 0) sh.wtot[0][wave] = S;
+        __syncthreads();
+        for (int w = wave + 1; w < NW; ++w) S += sh.wtot[0][w];
+        const uint32_t E = S - sum;
+        if (E < (uint32_t)need && S >= (uint32_t)need) {
+            uint32_t c = E;
+            int bsel = 0;
+#pragma unroll
+            for (int j = BPT - 1; j >= 0; --j) {
+                if (c + h[j] >= (uint32_t)need) {
+                    bsel = j;
+                    break;
                 }
-                sh.sh_bin = (kBins / kWave) * lane + bsel;
-                sh.sh_above = c;
+                c += h[j];
             }
+            sh.sh_bin = BPT * tid + bsel;
+            sh.sh_above = c;
         }
         __syncthreads();
         prefix |= (uint32_t)sh.sh_bin << shift;
@@ -104,7 +130,7 @@ __device__ uint32_t block_select(Sh &sh, int n, int need, Get get, uint32_t *abo
 // Shared memory of split_bound for a 256-thread block.
 struct BoundShared {
     uint32_t ukey[256 * kLocal];
-    uint32_t hist[kBins];
+    alignas(16) uint32_t hist[kBins];   // read as 16-byte vectors
     uint32_t wtot[2][256 / kWave];
     int sh_bin;
     uint32_t sh_above;

@@ -47,7 +47,7 @@ struct TopkShared {
     uint32_t ukey[kUnion];          // step 1 union, then reused
     uint32_t ckey[kCandCap];        // candidates: key
     int32_t cidx[kCandCap];         //             index
-    uint32_t hist[kBins];
+    alignas(16) uint32_t hist[kBins];   // read as 8-byte vectors
     uint32_t wtot[2][kWaves];
     int sh_bin;
     uint32_t sh_above;
