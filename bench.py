@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the retention-ratio sweep")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle wall time")
     ap.add_argument("--profile-only", action="store_true", help="run warmup+steps of the headline only")
-    ap.add_argument("--profile", choices=["prefill", "decode", "mla_prefill", "copy"],
+    ap.add_argument("--profile", choices=["prefill", "decode", "mla_prefill", "chunk", "copy"],
                     help="run warmup+steps of one workload (for profiler runs) and exit")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="HBM traffic per launch from rocprofv3 counter runs in DIR (subdirectories fetch/, "
@@ -239,11 +239,11 @@ def decode(args, torch, sa, inputs):
     }
 
 
-def serving_prefill_chunk(args, torch, sa, inputs):
-    """A serving batch holding one prefill chunk: the last 4096 positions of a
-    200,000-token sequence, its indexer keys in 64-row pages at random slots of
-    a pool.  Timed through idx_score_topk_paged (the fused kernel with page
-    lookups) next to idx_score_topk on the same rows over contiguous keys."""
+def _prefill_chunk_calls(torch, sa, inputs):
+    """Inputs of a serving batch holding one prefill chunk (the last 4096
+    positions of a 200,000-token sequence, its indexer keys in 64-row pages at
+    random slots of a pool) and two calls on them: idx_score_topk_paged (the
+    fused kernel with page lookups) and idx_score_topk over contiguous keys."""
     import dataclasses
     base = inputs.WORKLOADS["decode_200k"]
     C, L = 4096, base.Lk
@@ -264,12 +264,19 @@ def serving_prefill_chunk(args, torch, sa, inputs):
     wsp = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     tp = torch.empty(C, wl.topk, dtype=torch.int32, device=dev)
     tc = torch.empty(1, C, wl.topk, dtype=torch.int32, device=dev)
-    ms_paged = time_steps(lambda: sa.idx_score_topk_paged(qp, k_pool, table, qs, sl, wp, wl.topk, L, t_out=tp,
-                                                          ws=wsp), 5, 1, torch)
-    ms_contig = time_steps(lambda: sa.idx_score_topk(q, k, w, wl.topk, t_out=tc), 5, 1, torch)
+    paged = lambda: sa.idx_score_topk_paged(qp, k_pool, table, qs, sl, wp, wl.topk, L, t_out=tp, ws=wsp)
+    contig = lambda: sa.idx_score_topk(q, k, w, wl.topk, t_out=tc)
+    return paged, contig, tp, tc, (C, L, bs, ws_bytes)
+
+
+def serving_prefill_chunk(args, torch, sa, inputs):
+    """The prefill-chunk serving batch timed through idx_score_topk_paged next
+    to idx_score_topk on the same rows over contiguous keys."""
+    paged, contig, tp, tc, (C, L, bs, ws_bytes) = _prefill_chunk_calls(torch, sa, inputs)
+    ms_paged = time_steps(paged, 5, 1, torch)
+    ms_contig = time_steps(contig, 5, 1, torch)
     same = bool(torch.equal(tp, tc[0]))
     pairs = causal_pairs(C, L)
-    del k_pool
     return {"chunk_queries": C, "context": L, "block_size": bs, "pages": "random slots of one pool",
             "paged_ms": round(ms_paged, 3), "contiguous_ms": round(ms_contig, 3),
             "paged_pairs_per_s": round(pairs / (ms_paged * 1e-3), 1), "t_identical_to_contiguous": same,
@@ -379,6 +386,11 @@ def profile_run(args, torch, sa, inputs):
         out = torch.empty(wl.B, wl.Lq, wl.Hq, wl.Dv, dtype=torch.bfloat16, device=dev)
         for _ in range(args.warmup + args.steps):
             sa.sparse_mla_attn(qa, kv, t, 1.0 / math.sqrt(wl.Dqk), wl.Dv, out=out)
+    elif args.profile == "chunk":
+        paged, contig = _prefill_chunk_calls(torch, sa, inputs)[:2]
+        for _ in range(args.warmup + args.steps):
+            paged()
+            contig()
     else:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
