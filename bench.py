@@ -558,7 +558,7 @@ def main():
         traffic_from(args)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
     import torch

@@ -47,7 +47,7 @@ typedef enum {
     IDXC_ERR_SHAPE = -2,       /* a size is out of range or sizes disagree */
     IDXC_ERR_DTYPE = -3,       /* unknown encoding or unsupported encoding combination */
     IDXC_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
-    IDXC_ERR_UNSUPPORTED = -5, /* valid request this build has no kernel for */
+    IDXC_ERR_UNSUPPORTED = -5, /* valid request that no kernel of the library serves */
     IDXC_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required */
     IDXC_ERR_PATTERN = -7,     /* layer pattern invalid (see idx_cache_route) */
     IDXC_ERR_HIP = -8,         /* the HIP runtime reported an error at launch */
