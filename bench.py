@@ -209,6 +209,7 @@ def decode(args, torch, sa, inputs):
     same_t = bool(torch.equal(tp, t.view(wl.B, wl.topk)))
     del k_pool, kv_pool
     gathered = wl.B * wl.Lq * wl.topk * wl.Dqk * 2
+    ceiling = gather_ceiling(torch, sa, kv, t, wl, timed, gathered)
     key_bytes = wl.B * wl.Lk * wl.D
     tok = wl.B * wl.Lq
     layer_bytes = decode_layer_bytes(wl)
@@ -229,6 +230,8 @@ def decode(args, torch, sa, inputs):
         "indexer_key_read_GBs": round(key_bytes / (t_idx * 1e-3) / 1e9, 1),
         "gather_GBs": round(gathered / (t_att * 1e-3) / 1e9, 1),
         "gather_frac_hbm": round(gathered / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "gather_ceiling": ceiling,
+        "gather_frac_of_ceiling": round(gathered / (t_att * 1e-3) / 1e9 / ceiling["cold_GBs"], 4),
         "note": "cold: a read-only pass over 512 MB before each timed call; warm: back to back; one layer = one call each",
         "serving_paged": {
             "block_size": bs, "pages": "random slots of one pool, shared block table",
@@ -237,6 +240,37 @@ def decode(args, torch, sa, inputs):
             "t_identical_to_contiguous": same_t,
         },
     }
+
+
+def gather_ceiling(torch, sa, kv, t, wl, timed, gathered):
+    """GB/s of reading exactly the latent rows the decode step's T names
+    (idxc_calib_gather_rate: the same rows, 16-byte loads laid out as the
+    sparse attention copies them, nothing else to do), cold and warm, best
+    over a few grid sizes: what this pattern of random 1152-byte rows allows
+    on this part, next to the sparse attention kernel's own gather rate."""
+    import ctypes
+    assert wl.Lq == 1, "one query per sequence: query b reads rows of sequence b"
+    f = sa.lib().idxc_calib_gather_rate
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    shapes = (256, 512, 1024, 2048, 4096)
+    out = torch.empty(max(shapes) * 256, dtype=torch.int32, device=kv.device)
+    per = {}
+    for blocks in shapes:
+        def launch(blocks=blocks):
+            rc = f(kv.data_ptr(), wl.Dqk * 2, wl.Lk, t.data_ptr(), wl.B * wl.Lq, wl.topk, blocks, out.data_ptr(),
+                   torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"idxc_calib_gather_rate failed: {rc}")
+        per[blocks] = (gathered / (timed(launch) * 1e-3) / 1e9, gathered / (timed(launch, cold=False) * 1e-3) / 1e9)
+    bc = max(per, key=lambda b: per[b][0])
+    bw = max(per, key=lambda b: per[b][1])
+    return {"kernel": "idxc_calib_gather_rate", "rows": "the decode step's T over its latent cache, 1152-byte rows",
+            "cold_GBs": round(per[bc][0], 1), "warm_GBs": round(per[bw][1], 1),
+            "blocks_cold": bc, "blocks_warm": bw, "threads_per_block": 256,
+            "cold_frac_hbm": round(per[bc][0] / PEAK_HBM_GBS, 4),
+            "per_blocks_cold_warm_GBs": {str(b): [round(v[0], 1), round(v[1], 1)] for b, v in per.items()}}
 
 
 def _prefill_chunk_calls(torch, sa, inputs):

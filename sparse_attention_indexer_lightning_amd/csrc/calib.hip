@@ -1,5 +1,7 @@
-// calib.hip -- dense MFMA chains on caller-given operand bytes (measurement
-// support: the MFMA rate the benchmark's own operands allow on this part).
+// calib.hip -- measurement support: dense MFMA chains on caller-given operand
+// bytes (the MFMA rate the benchmark's own operands allow on this part), and
+// a plain gather of the rows an index set names (the HBM rate that pattern of
+// rows allows, with no computation behind the loads).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -62,7 +64,70 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     out[t] = s;
 }
 
+// Gather of the rows named by t (query b, entry j: row b * rows_per_seq +
+// t[b * k + j]), in the layout the sparse attention copies use: a wavefront
+// takes 8 consecutive entries, lane l reads 16-byte piece l % 8 of every
+// 128-byte line of entry l / 8's row, all LINES loads of a row group in
+// flight together; the next group's index is loaded before this group's
+// rows.  Entries outside [0, rows_per_seq) are skipped (their loads read row
+// 0 and are discarded, so every group issues the same loads).  Each thread
+// writes the XOR of the 32-bit words it used.
+template <int LINES>
+__global__ __launch_bounds__(kThreads) void gather_rate_kernel(const unsigned char *rows, long long rows_per_seq,
+                                                               const int32_t *t, int k, int n_entries, uint32_t *out) {
+    constexpr int kWaves = kThreads / 64;
+    constexpr size_t kRowBytes = 128 * LINES;
+    const int lane = threadIdx.x % 64;
+    const int wave = (int)blockIdx.x * kWaves + (int)threadIdx.x / 64;
+    const int nwaves = (int)gridDim.x * kWaves;
+    const int ngroups = (n_entries + 7) / 8;
+    const int sub = lane / 8, piece = 16 * (lane % 8);
+    auto index_of = [&](int g) { return t[min(8 * g + sub, n_entries - 1)]; };
+    uint32_t acc = 0;
+    int ix = index_of(min(wave, ngroups - 1));
+    for (int g = wave; g < ngroups; g += nwaves) {
+        const int ix_next = index_of(min(g + nwaves, ngroups - 1));
+        const int e = 8 * g + sub;
+        const bool ok = e < n_entries && ix >= 0 && (long long)ix < rows_per_seq;
+        const long long r = ok ? (long long)(e / k) * rows_per_seq + ix : 0;
+        const unsigned char *src = rows + (size_t)r * kRowBytes + piece;
+        v4i v[LINES];
+#pragma unroll
+        for (int q = 0; q < LINES; ++q) v[q] = *reinterpret_cast<const v4i *>(src + 128 * q);
+        uint32_t x = 0;
+#pragma unroll
+        for (int q = 0; q < LINES; ++q) x ^= (uint32_t)(v[q][0] ^ v[q][1] ^ v[q][2] ^ v[q][3]);
+        acc ^= ok ? x : 0u;
+        ix = ix_next;
+    }
+    out[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+template <int LINES>
+void launch_gather(int lines, dim3 grid, hipStream_t st, const unsigned char *rows, long long rows_per_seq,
+                   const int32_t *t, int k, int n_entries, uint32_t *out) {
+    if constexpr (LINES <= 16) {
+        if (lines == LINES)
+            hipLaunchKernelGGL(gather_rate_kernel<LINES>, grid, dim3(kThreads), 0, st, rows, rows_per_seq, t, k,
+                               n_entries, out);
+        else
+            launch_gather<LINES + 1>(lines, grid, st, rows, rows_per_seq, t, k, n_entries, out);
+    }
+}
+
 }  // namespace
+
+extern "C" int idxc_calib_gather_rate(const void *rows, size_t row_bytes, long long rows_per_seq, const int32_t *t,
+                                      int nq, int k, int blocks, uint32_t *out, void *stream) {
+    if (!rows || !t || !out) return IDXC_ERR_NULL;
+    if (row_bytes % 128 != 0 || row_bytes < 128 || row_bytes > 16 * 128 || rows_per_seq < 1 || nq < 1 || k < 1 ||
+        blocks < 1 || blocks > (1 << 20) || (long long)nq * k > (1ll << 30))
+        return IDXC_ERR_SHAPE;
+    if (((uintptr_t)rows | (uintptr_t)out) & 15u || (uintptr_t)t & 3u) return IDXC_ERR_ALIGN;
+    launch_gather<1>((int)(row_bytes / 128), dim3(blocks), static_cast<hipStream_t>(stream),
+                     static_cast<const unsigned char *>(rows), rows_per_seq, t, k, nq * k, out);
+    return hipGetLastError() == hipSuccess ? IDXC_OK : IDXC_ERR_HIP;
+}
 
 extern "C" int idxc_calib_mfma_rate(int kind, const void *a, size_t a_bytes, const void *b, size_t b_bytes, int iters,
                                     int blocks, float *out, void *stream) {

@@ -34,7 +34,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     L = sa.lib()
     names = declared_functions()
-    assert {"idx_score_topk", "idx_topk", "idx_cache_route", "sparse_mla_attn", "idxc_calib_mfma_rate"} <= set(names)
+    assert {"idx_score_topk", "idx_topk", "idx_cache_route", "sparse_mla_attn", "idxc_calib_mfma_rate",
+            "idxc_calib_gather_rate"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert L.idxc_abi_version() == 1
@@ -487,3 +488,26 @@ def test_calib_rejects_before_launch():
     assert f(1, FAKE, 64, FAKE, 64, 1, 0, FAKE, None) == SHAPE
     assert f(0, FAKE_ODD, 64, FAKE, 64, 1, 1, FAKE, None) == ALIGN
     assert f(2, FAKE, 64, FAKE, 64, 1, 1, FAKE, None) == DTYPE
+
+
+def test_calib_gather_rejects_before_launch():
+    L = sa.lib()
+    f = L.idxc_calib_gather_rate
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 1152, 10, FAKE, 1, 8, 1, FAKE, None) == NULL
+    assert f(FAKE, 1152, 10, None, 1, 8, 1, FAKE, None) == NULL
+    assert f(FAKE, 1152, 10, FAKE, 1, 8, 1, None, None) == NULL
+    assert f(FAKE, 1100, 10, FAKE, 1, 8, 1, FAKE, None) == SHAPE     # not whole 128-byte lines
+    assert f(FAKE, 0, 10, FAKE, 1, 8, 1, FAKE, None) == SHAPE
+    assert f(FAKE, 17 * 128, 10, FAKE, 1, 8, 1, FAKE, None) == SHAPE
+    assert f(FAKE, 1152, 0, FAKE, 1, 8, 1, FAKE, None) == SHAPE
+    assert f(FAKE, 1152, 10, FAKE, 0, 8, 1, FAKE, None) == SHAPE
+    assert f(FAKE, 1152, 10, FAKE, 1, 0, 1, FAKE, None) == SHAPE
+    assert f(FAKE, 1152, 10, FAKE, 1, 8, 0, FAKE, None) == SHAPE
+    assert f(FAKE, 1152, 10, FAKE, 1, 8, (1 << 20) + 1, FAKE, None) == SHAPE
+    assert f(FAKE, 1152, 10, FAKE, 1 << 16, 1 << 15, 1, FAKE, None) == SHAPE   # 2^31 entries
+    assert f(FAKE_ODD, 1152, 10, FAKE, 1, 8, 1, FAKE, None) == ALIGN
+    assert f(FAKE, 1152, 10, FAKE, 1, 8, 1, FAKE_ODD, None) == ALIGN
+    assert f(FAKE, 1152, 10, ctypes.c_void_p(0x10002), 1, 8, 1, FAKE, None) == ALIGN
