@@ -772,7 +772,10 @@ __host__ __device__ inline PrefillLds prefill_lds(int waves, int tw, int pitch, 
     return L;
 }
 
-template <Enc E, int D, int H, typename IdxT, bool Paged>
+// Var: bit 0 set when a score row may be written for tests (p.scores), bit 1
+// when keys may extend past 65,536 (segment table); launches without either
+// run a body with those per-block checks compiled out.
+template <Enc E, int D, int H, typename IdxT, bool Paged, int Var>
 __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void prefill_kernel(PrefillParams p) {
     using S = Shape<E, D>;
     constexpr int TW = 64 / H;              // query rows per wave
@@ -783,6 +786,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     // plan always gives with 16-bit candidate indices (keys up to 65536, or up
     // to kMaxSeg * 65536 with the segment table)
     constexpr bool kPipe = kMfma32 && sizeof(IdxT) == 2;
+    constexpr bool kDbg = (Var & 1) != 0, kSeg = (Var & 2) != 0;
     const int waves = p.nthreads / kWave;
     const int R = waves * TW;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave, g = lane >> 4,
@@ -894,7 +898,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
     const int want_level = p.topk + (p.cap - p.topk) / 4;   // past a quarter of the slack
     // segment table of this wave's row (pipelined sweep with keys beyond 65536)
     int *segs = reinterpret_cast<int *>(smem + L.segs) + wave * kMaxSeg;
-    const int nseg = kPipe ? (Lk + 65535) >> 16 : 1;
+    const int nseg = kPipe && kSeg ? (Lk + 65535) >> 16 : 1;
     auto seg_reset = [&]() {   // an empty buffer: every segment not reached yet
         if (nseg > 1) {
             wave_lds_order();
@@ -949,7 +953,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         const int pos = off + i;
         if (i >= Lq || base > pos) return false;
         const int s = base + lane;
-        if (p.scores) {   // the full score row, for tests only
+        if (kDbg && p.scores) {   // the full score row, for tests only
             if (s < Lk) p.scores[(row0 + i) * Lk + s] = s <= pos ? sc : -INFINITY;
         }
         const bool cand = s <= pos && sc > st.thr_f;
@@ -1331,7 +1335,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
                     if (base > pos) continue;
                     const int s = base + lane;
                     const int row = wave * TW + t;
-                    if (p.scores && s < Lk)
+                    if (kDbg && p.scores && s < Lk)
                         p.scores[(row0 + i) * Lk + s] = s <= pos ? sc[t] : -INFINITY;
                     int cnt = rcnt[row];
                     uint32_t thr = rthr[row];
@@ -1383,7 +1387,7 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             }
             o[j] = v;
         }
-        if (p.scores) {
+        if (kDbg && p.scores) {
             const int pos = off + i;
             for (int s = (pos / KB + 1) * KB + lane; s < Lk; s += kWave)
                 p.scores[(row0 + i) * Lk + s] = -INFINITY;
@@ -1601,10 +1605,10 @@ void decode_scores_kernel(ScoreParams p) {
     write_bound();
 }
 
-template <Enc E, int D, int H, typename IdxT, bool Paged = false>
-hipError_t launch_prefill_t(const IndexerArgs &a, int waves, int cap, size_t lds, hipStream_t st,
-                            const PagedPrefill *pp = nullptr) {
-    auto kern = prefill_kernel<E, D, H, IdxT, Paged>;
+template <Enc E, int D, int H, typename IdxT, bool Paged, int Var>
+hipError_t launch_prefill_v(const IndexerArgs &a, int waves, int cap, size_t lds, hipStream_t st,
+                            const PagedPrefill *pp) {
+    auto kern = prefill_kernel<E, D, H, IdxT, Paged, Var>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -1635,6 +1639,25 @@ hipError_t launch_prefill_t(const IndexerArgs &a, int waves, int cap, size_t lds
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(waves * kWave), lds, st, p);
     return hipGetLastError();
+}
+
+// The pipelined sweep (fp8, 64 heads, 128 dims, 16-bit candidates) comes in
+// four variants (score row for tests or not, keys past 65,536 or not); the
+// other kernels keep one body that checks both at run time.
+template <Enc E, int D, int H, typename IdxT, bool Paged = false>
+hipError_t launch_prefill_t(const IndexerArgs &a, int waves, int cap, size_t lds, hipStream_t st,
+                            const PagedPrefill *pp = nullptr) {
+    if constexpr (E == Enc::FP8 && D == 128 && H == 64 && sizeof(IdxT) == 2) {
+        const int var = (a.scores ? 1 : 0) | (a.Lk > 65536 ? 2 : 0);
+        switch (var) {
+        case 0: return launch_prefill_v<E, D, H, IdxT, Paged, 0>(a, waves, cap, lds, st, pp);
+        case 1: return launch_prefill_v<E, D, H, IdxT, Paged, 1>(a, waves, cap, lds, st, pp);
+        case 2: return launch_prefill_v<E, D, H, IdxT, Paged, 2>(a, waves, cap, lds, st, pp);
+        default: return launch_prefill_v<E, D, H, IdxT, Paged, 3>(a, waves, cap, lds, st, pp);
+        }
+    } else {
+        return launch_prefill_v<E, D, H, IdxT, Paged, 3>(a, waves, cap, lds, st, pp);
+    }
 }
 
 struct PrefillPlan {
