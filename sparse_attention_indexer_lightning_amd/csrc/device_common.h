@@ -20,7 +20,9 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+// the builtin takes the predicate as a lane mask (the HIP wrapper takes an
+// int, which makes the compiler materialise a comparison result first)
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // LDS instructions of one wavefront execute in issue order, so a later LDS
 // read sees an earlier LDS write by any lane of the same wavefront as long

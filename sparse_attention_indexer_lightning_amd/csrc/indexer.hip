@@ -76,6 +76,9 @@ constexpr int kHistWords = 320;  // 256 bins + one dummy slot per lane for maske
 // segments, keys up to kMaxSeg * 65536), and an index is its low 16 bits plus
 // the segment of its position.
 constexpr int kMaxSeg = 16;
+// Fourth word of a raw buffer descriptor on gfx9-family parts (32-bit data
+// format; no stride, no swizzle), as the loads of the pipelined sweep use it.
+constexpr int kBufferWord3 = 0x00020000;
 // Sampled starting threshold of the 64-head sweep: every kSampleStride-th key
 // block is scored first; a row's threshold is then its sample's r-th largest
 // key, r = ceil(7/4 * k * (sampled keys) / (keys)), unless r is below
@@ -956,8 +959,10 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         if (kDbg && p.scores) {   // the full score row, for tests only
             if (s < Lk) p.scores[(row0 + i) * Lk + s] = s <= pos ? sc : -INFINITY;
         }
-        const bool cand = s <= pos && sc > st.thr_f;
-        const uint64_t m = ballot(cand);
+        // one ballot per comparison (each compare writes its lane mask
+        // directly), and the mask feeds the write predicate (inverse ballot),
+        // so the candidate test is never kept as a per-lane value
+        const uint64_t m = ballot(s <= pos) & ballot(sc > st.thr_f);
         if (m) {
             uint32_t *bk = bkey_all + (size_t)wave * p.cap;
             IdxT *bi = bidx_all + (size_t)wave * p.cap;
@@ -974,7 +979,12 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             }
             const int at = st.cnt + lanes_below(m);
             const uint32_t key = score_key(sc);
-            if (cand) {
+            // the mask as an opaque scalar value: the compiler would otherwise
+            // fold the inverse ballot back into the comparison and carry that
+            // across the branch as a per-lane value
+            uint64_t mw = m;
+            asm volatile("" : "+s"(mw));
+            if (__builtin_amdgcn_inverse_ballot_w64(mw)) {
                 bk[at] = key;
                 bi[at] = (IdxT)s;
             }
@@ -1053,23 +1063,38 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
         const int krow = tid / CPK, kcol = (tid % CPK) * 16;
         auto fetch1c = [&](int blk, int kr) {
             const int key = min(blk * KB + kr, Lk - 1);   // past Lk: clamped, never used
-            // 32-bit offset from the sequence's base, or from the block's page
-            // (this sweep covers at most kMaxSeg * 65536 keys of 128 bytes,
-            // under 2^28 bytes): one VALU add instead of 64-bit address arithmetic
-            if constexpr (Paged) {
-                const unsigned char *pb = page_of(min(blk * KB, Lk - 1));
-                const uint32_t o = (uint32_t)(key & ((1 << p.bs_log2) - 1)) * (uint32_t)S::ROWB + (uint32_t)kcol;
-                return *reinterpret_cast<const v4i *>(pb + o);
-            } else {
-                const uint32_t o = (uint32_t)key * (uint32_t)S::ROWB + (uint32_t)kcol;
-                return *reinterpret_cast<const v4i *>(kseq + o);
-            }
+            // 32-bit offset from the block's page (one VALU add instead of
+            // 64-bit address arithmetic)
+            const unsigned char *pb = page_of(min(blk * KB, Lk - 1));
+            const uint32_t o = (uint32_t)(key & ((1 << p.bs_log2) - 1)) * (uint32_t)S::ROWB + (uint32_t)kcol;
+            return *reinterpret_cast<const v4i *>(pb + o);
         };
         struct KR { v4i c[CPT]; };
+        // Contiguous keys: block blk is read through a buffer descriptor (scalar
+        // registers) whose base is the block's first key and whose size ends at
+        // the sequence's last key; the lane offsets are loop constants, and keys
+        // past the sequence read as zero (the hardware's range check; their
+        // scores are masked by position), so a block costs no address VALU.
+        uint32_t voff[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) voff[c] = (uint32_t)(krow + c * KROWS) * (uint32_t)S::ROWB + (uint32_t)kcol;
         auto fetch1 = [&](int blk) {
             KR r;
+            if constexpr (Paged) {
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) r.c[c] = fetch1c(blk, krow + c * KROWS);
+                for (int c = 0; c < CPT; ++c) r.c[c] = fetch1c(blk, krow + c * KROWS);
+            } else {
+                const int ub = __builtin_amdgcn_readfirstlane(blk);
+                // bytes from the block on (this sweep covers at most kMaxSeg * 65536
+                // keys of 128 bytes: 32-bit arithmetic)
+                const int rem = (Lk - min(ub * KB, Lk)) * S::ROWB;
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<unsigned char *>(kseq) + (size_t)ub * (KB * S::ROWB), (short)0,
+                    min(rem, KB * S::ROWB), kBufferWord3);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c)
+                    r.c[c] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
+            }
             return r;
         };
         // Key tile swizzle: the 32-byte half h of key row r (16-byte chunks
@@ -1176,7 +1201,8 @@ __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 
             }
             // block blk-1's selection (none before block 0: a base past every position)
             const float lin_prev = linbuf[(PAR ^ 1) * (kPipeWaves * KB) + lin_get];
-            const bool need = select_binned(combine(p0_prev, p1) + lin_prev, blk >= 1 ? bmap(blk - 1) * KB : Lk);
+            const int bprev = __builtin_amdgcn_readfirstlane(blk) - 1;   // uniform: scalar arithmetic
+            const bool need = select_binned(combine(p0_prev, p1) + lin_prev, bprev >= 0 ? bmap(bprev) * KB : Lk);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rf = 0; rf < 2; ++rf) a1[rf] = mfma_fp8_32x32x64(Q32f.a[rf][0], B[1][0], z);
