@@ -31,6 +31,10 @@ def compare_all_rows(q, k, w, topk, what, exact_sets=False):
     B, Lq = q.shape[:2]
     Lk = k.shape[1]
     t, scores = run_full(q, k, w, topk)
+    # the launch without the test-only score row (the production variant of
+    # the fused sweep) gives the same T
+    t_nodbg, _ = run_full(q, k, w, topk, dbg=False)
+    assert torch.equal(t, t_nodbg), what
     to, so = indexer_oracle(q, k, w, topk)
     rt = RTOL[enc_of(q)]
     check_scores(scores.cpu().numpy().reshape(B * Lq, Lk), so, rt, what)
@@ -87,6 +91,9 @@ def test_head_counts_and_dims(enc, H, D):
 
 @pytest.mark.parametrize("B,Lq,Lk,topk", [
     (1, 50, 50, 64),        # every row shorter than k: pure padding
+    (1, 40, 40, 8),         # one partial key block (keys past the end read as zeros)
+    (1, 64, 64, 64),        # exactly one key block, k = every key
+    (2, 65, 65, 33),        # one block and one key, batch
     (1, 777, 777, 100),     # ragged length, several key blocks
     (3, 130, 130, 17),      # batch
     (1, 300, 1000, 256),    # chunked prefill: queries at the end of a longer context
